@@ -1,0 +1,124 @@
+"""Seeded synthetic inputs for causal / sliding-window grouped-query attention.
+
+This module draws random tensors and rounds them to the element type; it holds none of
+attention's arithmetic. Both the fp64 oracle (through the tests and the bench's CPU leg)
+and the HIP path receive exactly the arrays produced here, so the two sides always see
+the same rounded bits.
+
+Workloads (shapes and distributions of the attention configurations this library is
+measured and checked on; no dataset is involved, every input is synthetic):
+
+  tiny-causal-f32        B=1, Hq=Hkv=2,  S=64,    D=64,  f32,  causal
+  small-mha-causal-bf16  B=4, Hq=Hkv=16, S=1024,  D=64,  bf16, causal
+  gqa64x8-s4096-d128     B=1, Hq=64, Hkv=8, S=4096,  D=128, bf16, causal, dO ~ N(0, 0.1^2)
+  swa-w1024-s8192        B=1, Hq=Hkv=16, S=8192,  D=64,  bf16, causal, window 1024
+  gqa64x8-s32768-d128    B=1, Hq=64, Hkv=8, S=32768, D=128, bf16, causal, Q and K
+                         multiplied per head by factors drawn U(0.5, 2)
+
+Draw order per workload: numpy.random.default_rng(seed); Q, K, V, dO as float32
+standard normals in that order (dO then scaled by its standard deviation); then, for the
+long-context workload only, one factor per query head and one per KV head. Every tensor
+is then rounded once to the element type (round-to-nearest-even for bf16).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool
+    window: int  # 0 = no window; W >= 1 = key j visible to query i iff i - W < j <= i
+    seed: int
+    do_std: float = 1.0
+    head_factor: bool = False  # multiply Q and K per head by U(0.5, 2) factors
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def shapes(self):
+        return ((self.B, self.Hq, self.S, self.D), (self.B, self.Hkv, self.S, self.D))
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("tiny-causal-f32", 1, 2, 2, 64, 64, "f32", True, 0, 1001),
+        Workload("small-mha-causal-bf16", 4, 16, 16, 1024, 64, "bf16", True, 0, 1002),
+        Workload("gqa64x8-s4096-d128", 1, 64, 8, 4096, 128, "bf16", True, 0, 1003, do_std=0.1),
+        Workload("swa-w1024-s8192", 1, 16, 16, 8192, 64, "bf16", True, 1024, 1004),
+        Workload("gqa64x8-s32768-d128", 1, 64, 8, 32768, 128, "bf16", True, 0, 1005,
+                 head_factor=True),
+    )
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32
+    arrays whose values are exactly representable in bfloat16. Inputs here are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    r = ((u + bias) & np.uint32(0xFFFF0000)).astype(np.uint32)
+    return r.view(np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of float32 values that are already bfloat16-representable."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    assert not np.any(u & np.uint32(0xFFFF)), "value is not bfloat16-representable"
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def to_elem(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    raise ValueError(f"unknown element type {dtype!r}")
+
+
+def make_inputs(w: Workload, *, seed: int | None = None, B: int | None = None,
+                Hq: int | None = None, Hkv: int | None = None, S: int | None = None,
+                D: int | None = None):
+    """Draw (q, k, v, do) for workload `w` (optionally overriding its shape or seed).
+
+    Returns float32 numpy arrays holding element-type-representable values:
+    q, do [B,Hq,S,D]; k, v [B,Hkv,S,D], all contiguous with D fastest."""
+    B = w.B if B is None else B
+    Hq = w.Hq if Hq is None else Hq
+    Hkv = w.Hkv if Hkv is None else Hkv
+    S = w.S if S is None else S
+    D = w.D if D is None else D
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    do = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    if w.do_std != 1.0:
+        do *= np.float32(w.do_std)
+    if w.head_factor:
+        cq = rng.uniform(0.5, 2.0, size=Hq).astype(np.float32)
+        ck = rng.uniform(0.5, 2.0, size=Hkv).astype(np.float32)
+        q *= cq[None, :, None, None]
+        k *= ck[None, :, None, None]
+    return tuple(to_elem(t, w.dtype) for t in (q, k, v, do))
+
+
+def random_tensor(shape, dtype: str, seed: int, std: float = 1.0) -> np.ndarray:
+    """One seeded N(0, std^2) tensor rounded to the element type (for ad-hoc test shapes)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return to_elem(x, dtype)

@@ -1,0 +1,345 @@
+"""Pins for the fp64 oracle: checks against facts the mathematics fixes, independent of the
+oracle's own code. Each pin takes the oracle module `A` (oracle.attention, or a copy with a
+planted mistake) and raises AssertionError when the oracle disagrees.
+
+Kinds of pin used (each chosen so a plausible mistake -- a dropped term, a wrong sign or index,
+a transposed operand, an off-by-one mask -- fails at least one of them):
+  * central finite differences of L = sum(O * dO) (the backward is the derivative of the forward);
+  * a scalar brute force on tiny inputs that takes the softmax derivative through its full
+    Jacobian instead of the rowsum(dO * O) shortcut;
+  * torch's own float64 scaled_dot_product_attention and autograd on the CPU (a library routine);
+  * closed forms: constant V, identical keys, window 1, zero queries, a hand-derived three-token case;
+  * invariants: probability rows sum to 1, sum_j dS_ij = 0, sum_j dV_j = sum_i dO_i, keys outside
+    a row's visible set cannot change that row.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rng_inputs(seed, B, Hq, Hkv, S, D, std=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, S, D)) * std
+    k = rng.standard_normal((B, Hkv, S, D)) * std
+    v = rng.standard_normal((B, Hkv, S, D))
+    do = rng.standard_normal((B, Hq, S, D))
+    return q, k, v, do
+
+
+def _loss(A, q, k, v, do, causal, window, scale):
+    O, _ = A.forward(q, k, v, causal, window, scale)
+    return float(np.sum(O * do))
+
+
+# ---------------------------------------------------------------- finite differences
+def pin_fd_every_entry(A, Hq=2, Hkv=2, S=16, D=8, window=0, seed=0, tol=1e-6):
+    """Central differences on every entry of Q, K and V (h = 1e-6, float64)."""
+    q, k, v, do = _rng_inputs(seed, 1, Hq, Hkv, S, D)
+    scale = 1.0 / math.sqrt(D)
+    dQ, dK, dV = A.backward(q, k, v, do, True, window, scale)
+    h = 1e-6
+    for name, x, g in (("Q", q, dQ), ("K", k, dK), ("V", v, dV)):
+        fd = np.zeros_like(x)
+        flat = x.reshape(-1)
+        for idx in range(flat.size):
+            old = flat[idx]
+            flat[idx] = old + h
+            lp = _loss(A, q, k, v, do, True, window, scale)
+            flat[idx] = old - h
+            lm = _loss(A, q, k, v, do, True, window, scale)
+            flat[idx] = old
+            fd.reshape(-1)[idx] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(fd - g)) / max(np.max(np.abs(fd)), 1e-30)
+        assert err <= tol, f"finite differences vs d{name}: max rel err {err:.3e} > {tol}"
+
+
+def pin_fd_sampled(A, seed=1, n_entries=256, n_dirs=16, tol=1e-6):
+    """Tiny causal f32-workload shape (B=1, Hq=Hkv=2, S=64, D=64): central differences on a
+    seeded sample of entries and along random directions, for each of Q, K, V."""
+    q, k, v, do = _rng_inputs(seed, 1, 2, 2, 64, 64)
+    scale = 1.0 / 8.0
+    dQ, dK, dV = A.backward(q, k, v, do, True, 0, scale)
+    rng = np.random.default_rng(seed + 100)
+    h = 1e-6
+    for name, x, g in (("Q", q, dQ), ("K", k, dK), ("V", v, dV)):
+        flat = x.reshape(-1)
+        gf = g.reshape(-1)
+        idxs = rng.choice(flat.size, size=n_entries, replace=False)
+        errs = []
+        for idx in idxs:
+            old = flat[idx]
+            flat[idx] = old + h
+            lp = _loss(A, q, k, v, do, True, 0, scale)
+            flat[idx] = old - h
+            lm = _loss(A, q, k, v, do, True, 0, scale)
+            flat[idx] = old
+            errs.append(abs((lp - lm) / (2 * h) - gf[idx]))
+        gscale = np.max(np.abs(gf))
+        err = max(errs) / gscale
+        assert err <= tol, f"sampled finite differences d{name}: {err:.3e}"
+        for _ in range(n_dirs):
+            dirn = rng.standard_normal(x.shape)
+            x0 = x.copy()
+            x[...] = x0 + h * dirn
+            lp = _loss(A, q, k, v, do, True, 0, scale)
+            x[...] = x0 - h * dirn
+            lm = _loss(A, q, k, v, do, True, 0, scale)
+            x[...] = x0
+            fd = (lp - lm) / (2 * h)
+            an = float(np.sum(g * dirn))
+            rel = abs(fd - an) / max(abs(an), 1e-12)
+            assert rel <= 1e-5, f"directional derivative d{name}: rel err {rel:.3e}"
+
+
+# ---------------------------------------------------------------- scalar brute force
+def _brute(q, k, v, do, causal, window, scale):
+    """Pure-Python loops; softmax derivative through the full Jacobian dP_k/dx_j = P_k (d_kj - P_j)."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    O = np.zeros(q.shape)
+    L = np.zeros((B, Hq, S))
+    dQ = np.zeros(q.shape)
+    dK = np.zeros(k.shape)
+    dV = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for i in range(S):
+                vis = [j for j in range(S)
+                       if (not causal or j <= i) and (window == 0 or i - j < window)]
+                x = {j: scale * sum(q[b, h, i, d] * k[b, g, j, d] for d in range(D)) for j in vis}
+                mx = max(x.values())
+                z = sum(math.exp(x[j] - mx) for j in vis)
+                p = {j: math.exp(x[j] - mx) / z for j in vis}
+                L[b, h, i] = mx + math.log(z)
+                for d in range(D):
+                    O[b, h, i, d] = sum(p[j] * v[b, g, j, d] for j in vis)
+                dp = {j: sum(do[b, h, i, d] * v[b, g, j, d] for d in range(D)) for j in vis}
+                dx = {j: sum(dp[kk] * p[kk] * ((1.0 if kk == j else 0.0) - p[j]) for kk in vis)
+                      for j in vis}
+                for j in vis:
+                    for d in range(D):
+                        dQ[b, h, i, d] += scale * dx[j] * k[b, g, j, d]
+                        dK[b, g, j, d] += scale * dx[j] * q[b, h, i, d]
+                        dV[b, g, j, d] += p[j] * do[b, h, i, d]
+    return O, L, dQ, dK, dV
+
+
+def pin_bruteforce(A, tol=1e-12):
+    for (B, Hq, Hkv, S, D, causal, window, seed) in (
+        (1, 2, 2, 7, 3, True, 0, 3), (2, 4, 2, 9, 4, True, 3, 4), (1, 3, 1, 6, 2, False, 0, 5),
+        (1, 4, 4, 8, 5, True, 1, 6), (1, 2, 1, 5, 3, True, 9, 7),
+    ):
+        q, k, v, do = _rng_inputs(seed, B, Hq, Hkv, S, D)
+        scale = 0.7
+        r = A.forward_backward(q, k, v, do, causal, window, scale)
+        ref = _brute(q, k, v, do, causal, window, scale)
+        for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"),
+                              (r["O"], r["LSE"], r["dQ"], r["dK"], r["dV"]), ref):
+            err = np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30)
+            assert err <= tol, f"brute force {name} (S={S}, W={window}, causal={causal}): {err:.3e}"
+
+
+# ---------------------------------------------------------------- library routine
+def pin_torch_sdpa(A, tol=1e-12):
+    """torch.nn.functional.scaled_dot_product_attention in float64 on the CPU, K/V repeated
+    over contiguous head groups, gradients through autograd."""
+    import torch
+    for (B, Hq, Hkv, S, D, causal, window, seed) in (
+        (2, 4, 2, 33, 16, True, 0, 11), (1, 8, 2, 40, 8, True, 7, 12), (1, 2, 2, 24, 8, False, 0, 13),
+    ):
+        q, k, v, do = _rng_inputs(seed, B, Hq, Hkv, S, D)
+        scale = 1.0 / math.sqrt(D)
+        r = A.forward_backward(q, k, v, do, causal, window, scale)
+        G = Hq // Hkv
+        tq = torch.tensor(q, requires_grad=True)
+        tk = torch.tensor(k, requires_grad=True)
+        tv = torch.tensor(v, requires_grad=True)
+        i = torch.arange(S)[:, None]
+        j = torch.arange(S)[None, :]
+        mask = torch.ones(S, S, dtype=torch.bool)
+        if causal:
+            mask &= j <= i
+        if window:
+            mask &= (i - j) < window
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1),
+            attn_mask=mask, scale=scale)
+        o.backward(torch.tensor(do))
+        for name, x, y in (("O", r["O"], o.detach().numpy()), ("dQ", r["dQ"], tq.grad.numpy()),
+                           ("dK", r["dK"], tk.grad.numpy()), ("dV", r["dV"], tv.grad.numpy())):
+            err = np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30)
+            assert err <= tol, f"torch sdpa {name} (Hq={Hq}, Hkv={Hkv}, W={window}): {err:.3e}"
+
+
+# ---------------------------------------------------------------- closed forms
+def pin_three_token_closed_form(A, tol=1e-14):
+    q = np.zeros((1, 1, 3, 2))
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, 3, 2))
+    k[0, 0, :, 0] = np.log([1.0, 2.0, 3.0])
+    v = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]]).reshape(1, 1, 3, 2)
+    do = np.zeros((1, 1, 3, 2))
+    do[..., 0] = 1.0
+    r = A.forward_backward(q, k, v, do, True, 0, 2.0)
+    n = 0
+    with open(os.path.join(HERE, "golden", "three_token_closed_form.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            name, idx, comp, expr = line.split(None, 3)
+            want = float(eval(expr, {"math": math}))  # fixture expressions are plain arithmetic
+            got = r[name][0, 0, int(idx)] if comp == "-" else r[name][0, 0, int(idx), int(comp)]
+            assert abs(got - want) <= tol * max(1.0, abs(want)), f"{name}[{idx},{comp}]: {got} != {want}"
+            n += 1
+    assert n == 27
+
+
+def pin_constant_v(A):
+    q, k, v, do = _rng_inputs(21, 1, 4, 2, 37, 8)
+    v[:] = np.array([0.5, -1.0, 2.0, 0.0, 3.0, 1.0, -2.0, 0.25])
+    for window in (0, 1, 5):
+        O, _ = A.forward(q, k, v, True, window, 0.4)
+        assert np.max(np.abs(O - v[0, 0, 0])) <= 1e-14, f"constant V (W={window})"
+
+
+def pin_identical_keys(A):
+    """All keys equal => uniform weights over the visible set: O_i is the mean of the visible
+    V rows and LSE_i = s<q_i, k> + ln(#visible)."""
+    S, D = 50, 6
+    q, k, v, do = _rng_inputs(22, 1, 2, 1, S, D)
+    k[:] = k[0, 0, 0]
+    scale = 0.3
+    for window in (0, 1, 4, 64):
+        O, LSE = A.forward(q, k, v, True, window, scale)
+        for h in range(2):
+            for i in range(S):
+                lo = 0 if window == 0 else max(0, i - window + 1)
+                want = v[0, 0, lo:i + 1].mean(axis=0)
+                assert np.max(np.abs(O[0, h, i] - want)) <= 1e-13, f"identical keys O (W={window})"
+                wl = scale * float(q[0, h, i] @ k[0, 0, 0]) + math.log(i + 1 - lo)
+                assert abs(LSE[0, h, i] - wl) <= 1e-13, f"identical keys LSE (W={window})"
+
+
+def pin_window_one(A):
+    """W = 1: each query sees only its own key, so P = I, O_i = V_i, LSE_i = s<q_i, k_i>,
+    dV_j = sum over the group of dO_j, and dQ = dK = 0."""
+    q, k, v, do = _rng_inputs(23, 2, 4, 2, 19, 8)
+    r = A.forward_backward(q, k, v, do, True, 1, 0.5)
+    G = 2
+    for h in range(4):
+        g = h // G
+        assert np.max(np.abs(r["O"][:, h] - v[:, g])) <= 1e-14
+        lse = 0.5 * np.einsum("bsd,bsd->bs", q[:, h], k[:, g])
+        assert np.max(np.abs(r["LSE"][:, h] - lse)) <= 1e-13
+    dv = do.reshape(2, 2, G, 19, 8).sum(axis=2)
+    assert np.max(np.abs(r["dV"] - dv)) <= 1e-13
+    assert np.max(np.abs(r["dQ"])) <= 1e-13 and np.max(np.abs(r["dK"])) <= 1e-13
+
+
+def pin_zero_queries(A):
+    """Q = 0: every visible score is 0, so exp(LSE_i) is exactly the number of visible keys
+    (i+1 causal, min(i+1, W) with a window, S without the causal mask) and O_i is their mean."""
+    S, D = 70, 4
+    q, k, v, do = _rng_inputs(24, 1, 2, 2, S, D)
+    q[:] = 0.0
+    for causal, window in ((True, 0), (True, 1), (True, 63), (True, 64), (True, 65), (False, 0)):
+        O, LSE = A.forward(q, k, v, causal, window, 1.0)
+        i = np.arange(S)
+        if not causal:
+            count = np.full(S, S)
+        elif window == 0:
+            count = i + 1
+        else:
+            count = np.minimum(i + 1, window)
+        assert np.array_equal(np.rint(np.exp(LSE[0, 0])).astype(np.int64), count), (causal, window)
+
+
+# ---------------------------------------------------------------- invariants
+def pin_rows_sum_to_one(A):
+    q, k, v, do = _rng_inputs(25, 1, 4, 2, 45, 8, std=2.0)
+    for window in (0, 3, 17):
+        for h in range(4):
+            P = A.probabilities(q, k, 0, h, True, window, 0.5)
+            assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= 1e-14
+            i = np.arange(45)[:, None]
+            j = np.arange(45)[None, :]
+            hidden = (j > i) | ((window > 0) & (i - j >= window))
+            assert np.all(P[hidden] == 0.0) and np.all(P[~hidden] > 0.0)
+
+
+def pin_gradient_identities(A):
+    """sum_j dS_ij = 0 (softmax rows sum to a constant), hence sum_j dK_j = 0 per KV head;
+    sum_j dV_j = sum over the group's heads and rows of dO (probability rows sum to 1)."""
+    q, k, v, do = _rng_inputs(26, 2, 6, 2, 41, 8)
+    r = A.forward_backward(q, k, v, do, True, 9, 0.35)
+    assert np.max(np.abs(r["dK"].sum(axis=2))) <= 1e-12 * np.max(np.abs(r["dK"])) * 41
+    want = do.reshape(2, 2, 3, 41, 8).sum(axis=(2, 3))
+    assert np.max(np.abs(r["dV"].sum(axis=2) - want)) <= 1e-12
+    qh = q[0, 1]
+    t = A.head_rows(qh, k[0, 0], v[0, 0], np.arange(41), True, 9, 0.35, do[0, 1])
+    assert np.max(np.abs(t["dS"].sum(axis=1))) <= 1e-15 * 41 * np.max(np.abs(t["dP"]))
+    # delta_i equals <dO_i, O_i>
+    assert np.max(np.abs(t["delta"] - np.sum(do[0, 1] * t["O"], axis=1))) <= 1e-13
+
+
+def pin_gqa_is_repeated_mha(A):
+    """Grouped heads equal full multi-head attention with K/V repeated over contiguous groups;
+    dK/dV are the group sums of the multi-head dK/dV."""
+    q, k, v, do = _rng_inputs(27, 1, 8, 2, 23, 8)
+    r = A.forward_backward(q, k, v, do, True, 6, 0.5)
+    kr = np.repeat(k, 4, axis=1)
+    vr = np.repeat(v, 4, axis=1)
+    m = A.forward_backward(q, kr, vr, do, True, 6, 0.5)
+    for name in ("O", "LSE", "dQ"):
+        assert np.max(np.abs(r[name] - m[name])) <= 1e-14, name
+    assert np.max(np.abs(r["dK"] - m["dK"].reshape(1, 2, 4, 23, 8).sum(axis=2))) <= 1e-13
+    assert np.max(np.abs(r["dV"] - m["dV"].reshape(1, 2, 4, 23, 8).sum(axis=2))) <= 1e-13
+
+
+def pin_hidden_keys_do_not_matter(A):
+    """Changing K_j, V_j for keys no query in a row set can see leaves those rows' O, LSE and dQ
+    bitwise unchanged."""
+    S = 40
+    q, k, v, do = _rng_inputs(28, 1, 2, 2, S, 8)
+    for window, i0 in ((0, 17), (5, 30)):
+        r = A.forward_backward(q, k, v, do, True, window, 0.5)
+        k2, v2 = k.copy(), v.copy()
+        hidden = [j for j in range(S) if j > i0 or (window and i0 - j >= window)]
+        k2[:, :, hidden] += 3.0
+        v2[:, :, hidden] -= 5.0
+        r2 = A.forward_backward(q, k2, v2, do, True, window, 0.5)
+        assert np.array_equal(r["O"][:, :, i0], r2["O"][:, :, i0])
+        assert np.array_equal(r["LSE"][:, :, i0], r2["LSE"][:, :, i0])
+        assert np.array_equal(r["dQ"][:, :, i0], r2["dQ"][:, :, i0])
+
+
+def pin_row_and_column_helpers(A):
+    """The row/column helpers used for sampled checks at full size agree with the full pass."""
+    q, k, v, do = _rng_inputs(29, 2, 4, 2, 60, 8)
+    for window in (0, 11):
+        r = A.forward_backward(q, k, v, do, True, window, 0.4, row_block=16)
+        rows = np.array([0, 5, 31, 59])
+        O, LSE = A.rows_forward(q, k, v, 1, 3, rows, True, window, 0.4)
+        assert np.max(np.abs(O - r["O"][1, 3, rows])) <= 1e-14
+        assert np.max(np.abs(LSE - r["LSE"][1, 3, rows])) <= 1e-14
+        dq = A.rows_dq(q, k, v, do, 1, 3, rows, True, window, 0.4)
+        assert np.max(np.abs(dq - r["dQ"][1, 3, rows])) <= 1e-13
+        cols = np.array([0, 7, 58, 59])
+        dk, dv = A.cols_dkdv(q, k, v, do, 1, 1, cols, True, window, 0.4, row_block=7)
+        assert np.max(np.abs(dk - r["dK"][1, 1, cols])) <= 1e-13
+        assert np.max(np.abs(dv - r["dV"][1, 1, cols])) <= 1e-13
+
+
+ALL_PINS = [
+    pin_fd_every_entry, pin_bruteforce, pin_torch_sdpa, pin_three_token_closed_form,
+    pin_constant_v, pin_identical_keys, pin_window_one, pin_zero_queries, pin_rows_sum_to_one,
+    pin_gradient_identities, pin_gqa_is_repeated_mha, pin_hidden_keys_do_not_matter,
+    pin_row_and_column_helpers,
+]

@@ -1,0 +1,92 @@
+"""Planted mistakes in the oracle (CPU only): each plausible error must make at least one pin in
+oracle_pins.py fail. This shows the pins constrain the oracle rather than restate it."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.attention as A
+import oracle_pins as P
+
+_real_head_rows = A.head_rows
+_real_fb = A.forward_backward
+_real_mask = A.visible_mask
+
+
+def _head_rows_mut(kind):
+    def f(qh, kh, vh, rows, causal, window, scale, doh=None):
+        t = _real_head_rows(qh, kh, vh, rows, causal, window, scale, doh)
+        if doh is not None:
+            if kind == "dropped_delta":          # dS = P * dP (rowsum term dropped)
+                t["dS"] = t["P"] * t["dP"]
+            elif kind == "dS_sign":
+                t["dS"] = -t["dS"]
+            elif kind == "delta_from_wrong_axis":  # sum over rows instead of keys
+                d = (t["P"] * t["dP"]).sum(axis=0)[: len(rows)]
+                d = np.pad(d, (0, len(rows) - d.size))
+                t["dS"] = t["P"] * (t["dP"] - d[:, None])
+        if kind == "unnormalised_P":
+            t["P"] = t["P"] * 1.001
+        return t
+    return f
+
+
+def _fb_mut(kind):
+    def f(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256):
+        r = _real_fb(q, k, v, do, causal, window, scale, row_block)
+        s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+        if kind == "lse_base2":
+            r["LSE"] = r["LSE"] / math.log(2.0)
+        if do is not None:
+            if kind == "dq_missing_scale":
+                r["dQ"] = r["dQ"] / s
+            elif kind == "dk_transposed_groups":  # dK of KV heads swapped
+                r["dK"] = r["dK"][:, ::-1].copy()
+        return r
+    return f
+
+
+def _mask_mut(kind):
+    def f(rows, cols, causal, window):
+        i = np.asarray(rows, dtype=np.int64)[:, None]
+        j = np.asarray(cols, dtype=np.int64)[None, :]
+        m = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+        if causal:
+            m &= (j < i) | (j == i) if kind != "causal_transposed" else (j >= i)
+        if window > 0:
+            m &= ((i - j) <= window) if kind == "window_off_by_one" else ((i - j) < window)
+        return m
+    return f
+
+
+MUTANTS = {
+    "dropped_delta": ("head_rows", _head_rows_mut("dropped_delta")),
+    "dS_sign": ("head_rows", _head_rows_mut("dS_sign")),
+    "delta_from_wrong_axis": ("head_rows", _head_rows_mut("delta_from_wrong_axis")),
+    "unnormalised_P": ("head_rows", _head_rows_mut("unnormalised_P")),
+    "lse_base2": ("forward_backward", _fb_mut("lse_base2")),
+    "dq_missing_scale": ("forward_backward", _fb_mut("dq_missing_scale")),
+    "dk_transposed_groups": ("forward_backward", _fb_mut("dk_transposed_groups")),
+    "kv_head_interleaved": ("kv_head", lambda h, Hq, Hkv: h % Hkv),
+    "window_off_by_one": ("visible_mask", _mask_mut("window_off_by_one")),
+    "causal_transposed": ("visible_mask", _mask_mut("causal_transposed")),
+}
+
+# Pins that run quickly enough to try on every mutant.
+FAST_PINS = [p for p in P.ALL_PINS if p is not P.pin_torch_sdpa] + [P.pin_torch_sdpa]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(A, attr, fn)
+    if attr == "forward_backward":
+        # forward/backward/... reach forward_backward through the module, so they see it too
+        pass
+    caught = []
+    for pin in FAST_PINS:
+        try:
+            pin(A)
+        except (AssertionError, ValueError, IndexError) as e:  # a pin rejected the oracle
+            caught.append(f"{pin.__name__}: {str(e)[:80]}")
+    assert caught, f"planted mistake {name!r} passed every pin"
