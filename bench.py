@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Forward + backward causal GQA attention throughput on one MI355X.
+
+One step = attn_fwd then attn_bwd (delta preprocess, dK/dV kernel, dQ kernel) over one batch
+of synthetic input already resident in HBM. Default workload: B=1, Hq=64, Hkv=8, S=4096, D=128,
+bf16, causal. Prints one JSON line.
+
+FLOPs are counted as 4*B*Hq*N*D for the forward, with N = S^2/2 attended pairs under the causal
+mask (the exact pair count with a window, S^2 without a mask), and 2.5x that for the backward.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "fwd+bwd causal attn TFLOP/s & % bf16 MFMA peak (GQA 64/8, d128, S=4096)"
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd.hip", "device.h", "tiles.h"],
+    "attn_bwd_delta": ["attn_bwd.hip", "device.h"],
+    "attn_bwd_dkdv": ["attn_bwd.hip", "device.h", "tiles.h"],
+    "attn_bwd_dq": ["attn_bwd.hip", "device.h", "tiles.h"],
+}
+
+
+def attended_pairs(S: int, causal: bool, window: int) -> float:
+    if not causal:
+        return float(S) * S
+    if window == 0:
+        return S * S / 2.0
+    W = min(window, S)
+    return W * (W + 1) / 2.0 + (S - W) * W
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "causal_attention_fa2_amd", "csrc")
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, if they
+    were taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, do, heads: int):
+    """The fp64 oracle, timed on this host's cores, on the first `heads` query heads (whole KV
+    groups) of the same inputs."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the affinity mask instead
+        threads = len(os.sched_getaffinity(0))
+    G = w.Hq // w.Hkv
+    heads = max(G, min(w.Hq, heads // G * G))
+    groups = heads // G
+    t0 = time.perf_counter()
+    oracle.forward_backward(q[:, :heads], k[:, :groups], v[:, :groups], do[:, :heads],
+                            w.causal, w.window, w.scale)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.B * heads * attended_pairs(w.S, w.causal, w.window) * w.D * 3.5
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd on {heads} of {w.Hq} query heads ({groups} KV groups), "
+                      f"B={w.B}, S={w.S}, D={w.D}: {dt:.2f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa64x8-s4096-d128")
+    ap.add_argument("--cpu-heads", type=int, default=24,
+                    help="query heads in the CPU oracle sample (rounded to whole KV groups)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention library runs on a single MI355X "
+              "(no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import causal_attention_fa2_amd as fa
+    from causal_attention_fa2_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    q, k, v, do = make_inputs(w)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tq, tk, tv, tdo = (torch.from_numpy(x).to(td).cuda() for x in (q, k, v, do))
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    ws = torch.empty(fa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        fa.attn_fwd(tq, tk, tv, o, lse, w.causal, w.window, w.scale)
+        fa.attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window, w.scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps between two synchronisations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # per-kernel durations: HIP events recorded on the launch stream around each kernel
+    events = {}
+
+    def hook(kernel, after, stream):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(torch.cuda.current_stream())
+        events.setdefault(kernel, []).append(ev)
+
+    fa.attn_set_launch_hook(hook)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_hooked = (time.perf_counter() - t1) * 1e3 / args.steps
+    fa.attn_set_launch_hook(None)
+    kern_ms = {}
+    for name, evs in events.items():
+        d = [evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2)]
+        kern_ms[name] = sum(d) / len(d)
+
+    N = attended_pairs(w.S, w.causal, w.window)
+    unit = 2.0 * w.B * w.Hq * N * w.D  # one GEMM-sized pass over the attended pairs
+    fl = {"attn_fwd": 2 * unit, "attn_bwd_dkdv": 4 * unit, "attn_bwd_dq": 1 * unit}
+    total_flops = 7 * unit  # forward (2) + backward counted as 2.5x forward (5)
+    value = total_flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    eb = 2 if w.dtype == "bf16" else 4
+    delta_bytes = w.B * w.Hq * w.S * (2 * w.D * eb + 4)
+
+    kernels = {}
+    for name, t in kern_ms.items():
+        rec = {"avg_ms": round(t, 4)}
+        if name in fl:
+            rec["tflops"] = round(fl[name] / (t * 1e-3) / 1e12, 1)
+        else:
+            rec["gbs"] = round(delta_bytes / (t * 1e-3) / 1e9, 1)
+        kernels[name] = rec
+    dom = max(kern_ms, key=kern_ms.get)
+    if dom in fl:
+        ach = fl[dom] / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
+    else:
+        ach = delta_bytes / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = load_traffic(dom, w.name)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+                   "causal": w.causal, "window": w.window, "parallelism": "none (1 GPU)"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "ms_per_step_with_kernel_events": round(ms_hooked, 4),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

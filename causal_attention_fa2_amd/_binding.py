@@ -1,0 +1,190 @@
+"""ctypes binding of libattn.so: the C-ABI calls under the same names, taking torch tensors.
+
+Argument marshalling only: every step of the attention path runs in the HIP kernels behind
+the C ABI. torch supplies device memory (tensor.data_ptr()) and the stream
+(torch.cuda.current_stream().cuda_stream, a hipStream_t on ROCm). There is no fallback: if the
+library is missing or not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_DEVICE = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16 = 0, 1
+
+_lib = None
+_hook_ref = None
+
+# void (*)(const char* kernel, int after, void* stream, void* user)
+LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p)
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m causal_attention_fa2_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                             i, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = i
+    lib.attn_set_launch_hook.argtypes = [LAUNCH_HOOK, vp]
+    lib.attn_set_launch_hook.restype = None
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+status_string = attn_status_string
+
+
+def attn_abi_version() -> int:
+    return int(load_library().attn_abi_version())
+
+
+def attn_set_launch_hook(fn) -> None:
+    """fn(kernel: str, after: int, stream: int) is called just before (after=0) and just after
+    (after=1) each kernel the library enqueues; None removes it."""
+    global _hook_ref
+    lib = load_library()
+    if fn is None:
+        lib.attn_set_launch_hook(LAUNCH_HOOK(), None)
+        _hook_ref = None
+        return
+
+    def tramp(kernel, after, stream, user):
+        fn(kernel.decode(), int(after), int(stream or 0))
+
+    _hook_ref = LAUNCH_HOOK(tramp)  # keep the trampoline alive while the library holds it
+    lib.attn_set_launch_hook(_hook_ref, None)
+
+
+def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, D: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def attn_fwd(q, k, v, o, lse, causal: bool = True, window: int = 0, scale: float | None = None,
+             stream=None) -> None:
+    """Calls attn_fwd: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> o [B,Hq,S,D] (q's dtype), lse [B,Hq,S] f32."""
+    import torch
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _check_tensor("k", k, (B, Hkv, S, D), q.dtype, q.device)
+    _check_tensor("v", v, (B, Hkv, S, D), q.dtype, q.device)
+    _check_tensor("o", o, (B, Hq, S, D), q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, S), torch.float32, q.device)
+    if not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous GPU tensor")
+    scale = D ** -0.5 if scale is None else float(scale)
+    st = load_library().attn_fwd(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, S, D, int(bool(causal)),
+                                 int(window), scale, _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = True, window: int = 0,
+             scale: float | None = None, stream=None) -> None:
+    """Calls attn_bwd; dq/dk/dv are overwritten. workspace: a uint8 GPU tensor of at least
+    attn_bwd_workspace_bytes(...) bytes."""
+    import torch
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    for name, t, shp in (("k", k, (B, Hkv, S, D)), ("v", v, (B, Hkv, S, D)), ("o", o, (B, Hq, S, D)),
+                         ("dout", dout, (B, Hq, S, D)), ("dq", dq, (B, Hq, S, D)),
+                         ("dk", dk, (B, Hkv, S, D)), ("dv", dv, (B, Hkv, S, D))):
+        _check_tensor(name, t, shp, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, S), torch.float32, q.device)
+    if not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous GPU tensor")
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    scale = D ** -0.5 if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().attn_bwd(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                                 dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), nbytes,
+                                 B, Hq, Hkv, S, D, int(bool(causal)), int(window), scale,
+                                 _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+
+
+# ---------------------------------------------------------------- allocation conveniences
+def forward(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None, stream=None):
+    """Allocates o and lse with torch, then calls attn_fwd. Returns (o, lse)."""
+    import torch
+    B, Hq, S, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, causal, window, scale, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = True, window: int = 0,
+             scale: float | None = None, stream=None, workspace=None):
+    """Allocates dq, dk, dv (and the workspace if none is given), then calls attn_bwd."""
+    import torch
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if workspace is None:
+        workspace = torch.empty(max(1, attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)),
+                                dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale, stream)
+    return dq, dk, dv

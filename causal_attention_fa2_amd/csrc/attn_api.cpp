@@ -1,0 +1,128 @@
+// attn_api.cpp -- the extern "C" entry points declared in include/attn.h.
+//
+// Every argument check runs on the host before anything is enqueued, so a rejected call has no
+// side effects. Readings of the definition that the checks enforce: Hq must be a multiple of Hkv
+// (query heads split into equal contiguous groups, Grip paragraph of the "KYNETRA FOUNDRY" page);
+// window 0 means no window and a window needs the causal mask (the single window parameter of
+// "CUDA-LLM: A GitHub Repository for Development", section "The custom CUDA kernel", only ever
+// narrows causal attention).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn.h"
+#include "launch.h"
+
+namespace {
+
+attn_launch_hook_t g_hook = nullptr;
+void* g_hook_user = nullptr;
+
+int check_common(int dtype, int B, int Hq, int Hkv, int S, int D, int causal, int window,
+                 float scale) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return ATTN_ERR_INVALID;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
+  if (window < 0) return ATTN_ERR_INVALID;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
+  if (!causal && window > 0) return ATTN_ERR_UNSUPPORTED;
+  const int64_t elems = (int64_t)B * Hq * S * D;
+  if (elems >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+namespace fa {
+void notify_launch(const char* kernel, int after, void* stream) {
+  attn_launch_hook_t h = g_hook;
+  if (h) h(kernel, after, stream, g_hook_user);
+}
+}  // namespace fa
+
+extern "C" {
+
+void attn_set_launch_hook(attn_launch_hook_t hook, void* user) {
+  g_hook_user = user;
+  g_hook = hook;
+}
+
+
+int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+             int Hq, int Hkv, int S, int D, int causal, int window, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
+  int st = check_common(dtype, B, Hq, Hkv, S, D, causal, window, scale);
+  if (st != ATTN_OK) return st;
+  fa::Args a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.D = D;
+  a.causal = causal;
+  a.window = window;
+  a.scale = scale;
+  a.stream = stream;
+  return fa::launch_fwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
+  if (check_common(ATTN_BF16, B, Hq, Hkv, S, D, 1, 0, 1.0f) != ATTN_OK) return 0;
+  return fa::bwd_workspace_bytes(B, Hq, S);
+}
+
+int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int causal, int window,
+             float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return ATTN_ERR_INVALID;
+  int st = check_common(dtype, B, Hq, Hkv, S, D, causal, window, scale);
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, S)) return ATTN_ERR_INVALID;
+  fa::Args a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o_in = o;
+  a.lse = const_cast<float*>(lse);
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.D = D;
+  a.causal = causal;
+  a.window = window;
+  a.scale = scale;
+  a.stream = stream;
+  return fa::launch_bwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_DEVICE: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// attn_fwd.hip -- tiled causal / sliding-window GQA attention forward for gfx950.
+//
+// Method: "KYNETRA FOUNDRY" page, FlashAttention paragraph (query tiles stream key/value tiles
+// through on-chip memory with a running max and running sum, rescaling the output accumulator, so
+// the S x S matrix never reaches HBM); "CUDA-LLM: A GitHub Repository for Development", section
+// "The custom CUDA kernel" (one window parameter for full-causal and sliding-window; the
+// log-sum-exp is saved for the backward); Grip paragraph of the first page for the head groups.
+//
+// Work decomposition (one workgroup = NW waves = 32*NW query rows of one (batch, query head)):
+//   * each wave owns 32 query rows; its Q rows stay in registers for the whole kernel as the
+//     B operand of S^T = K Q^T (one accumulator column per query, so every lane owns one query:
+//     the row max / row sum are in-lane plus one permlane32 swap with the partner lane);
+//   * key / value tiles of 32*KB rows are copied into swizzled LDS tiles shared by the waves;
+//   * P^T stays in registers and is the B operand of O^T = V^T P^T; V^T comes from LDS with the
+//     gfx950 transposing read, so V is never transposed in memory;
+//   * key tiles outside a wave's causal / window band are skipped, only boundary tiles are masked;
+//   * softmax runs in base 2 (scale * log2 e folded into one multiply); lse is exported as ln.
+#include "device.h"
+#include "launch.h"
+
+namespace fa {
+
+template <class E, int D, int NW, int KB>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(
+    const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
+    const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
+    int B, int Hq, int Hkv, int S, int causal, int window, float scale_log2, int n_qt) {
+  constexpr int BR = 32 * NW;
+  constexpr int BC = 32 * KB;
+  constexpr int DS = D / 16;  // 16-wide contraction steps over the head dimension
+  constexpr int DB = D / 32;  // 32-wide output blocks over the head dimension
+  typedef LdsTile<E, BC, D> KvTile;
+  __shared__ __attribute__((aligned(16))) char smem[2 * KvTile::kBytes];
+  char* k_lds = smem;
+  char* v_lds = smem + KvTile::kBytes;
+
+  const int lane = lane_id();
+  const int w = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  // Heaviest query tiles first (causal work grows with the tile index); heads vary fastest.
+  const int BH = B * Hq;
+  const int rank = blockIdx.x / BH;
+  const int bh = blockIdx.x - rank * BH;
+  const int qt = causal ? n_qt - 1 - rank : rank;
+  const int b = bh / Hq;
+  const int h = bh - b * Hq;
+  const int g = h / (Hq / Hkv);
+
+  const typename E::T* q_bh = Q + (size_t)(b * Hq + h) * S * D;
+  const typename E::T* k_bg = K + (size_t)(b * Hkv + g) * S * D;
+  const typename E::T* v_bg = V + (size_t)(b * Hkv + g) * S * D;
+
+  const int q0 = qt * BR;
+  const int qw = q0 + 32 * w;  // first row of this wave
+  const int my_q = qw + l32;   // the query row this lane owns
+  const bool q_ok = my_q < S;
+
+  Frag<E> qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) qf[s] = load_frag_global(q_bh + (size_t)my_q * D + 16 * s + 8 * half, q_ok);
+
+  f32x16_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+  float m = kNegInf;  // running max of base-2 scores
+  float l = 0.f;      // running sum of exp2(score - m)
+
+  int jt_lo, jt_hi;
+  kv_tile_range(q0, imin_(q0 + BR - 1, S - 1), S, BC, causal, window, &jt_lo, &jt_hi);
+
+  for (int jt = jt_lo; jt <= jt_hi; ++jt) {
+    const int j0 = jt * BC;
+    __syncthreads();
+    load_tile<E, KvTile, BC, D, NW * 64>(k_lds, k_bg, j0, S);
+    load_tile<E, KvTile, BC, D, NW * 64>(v_lds, v_bg, j0, S);
+    __syncthreads();
+    if (block_empty(qw, qw + 31, j0, j0 + BC - 1, S, causal, window)) continue;
+    const bool full = block_full(qw, qw + 31, j0, j0 + BC - 1, S, causal, window);
+
+    // S^T = K Q^T for KB blocks of 32 keys: lane owns query my_q, registers hold keys.
+    f32x16_t st[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      st[kb] = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) mma(st[kb], RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s), qf[s]);
+    }
+
+    float tmax = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = st[kb][r] * scale_log2;
+        if (!full) {
+          const int j = j0 + 32 * kb + acc_row(r);
+          if (!visible(my_q, j, S, causal, window)) x = kNegInf;
+        }
+        st[kb][r] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    tmax = pair_max(tmax);
+    const float m_new = fmaxf(m, tmax);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;  // row with nothing visible yet
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(st[kb][r] - m_use);
+        st[kb][r] = p;
+        psum += p;
+      }
+    }
+    psum = pair_sum(psum);
+    l = l * alpha + psum;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+
+    // O^T += V^T P^T, contraction over the tile's keys in the accumulator's row order.
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const Frag<E> pf = acc_frag<E>(st[kb], t);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          mma(acc[db], TrFrag<E, KvTile>::get(v_lds, 32 * kb + 16 * t, 32 * db), pf);
+      }
+    }
+  }
+
+  if (!q_ok) return;
+  const float inv_l = 1.f / l;
+  typename E::T* o_row = O + ((size_t)(b * Hq + h) * S + my_q) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * db + 8 * r4 + 4 * half;  // registers 4*r4 .. 4*r4+3 hold d .. d+3
+      const float x0 = acc[db][4 * r4 + 0] * inv_l, x1 = acc[db][4 * r4 + 1] * inv_l;
+      const float x2 = acc[db][4 * r4 + 2] * inv_l, x3 = acc[db][4 * r4 + 3] * inv_l;
+      if constexpr (E::kBytes == 2) {
+        *reinterpret_cast<u32x2_t*>(o_row + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+      } else {
+        *reinterpret_cast<f32x4_t*>(o_row + d) = f32x4_t{x0, x1, x2, x3};
+      }
+    }
+  }
+  if (half == 0) LSE[(size_t)(b * Hq + h) * S + my_q] = (m + __log2f(l)) * kLn2;
+}
+
+template <class E, int D>
+static int launch_fwd_t(const Args& a) {
+  constexpr int NW = 4, KB = 2;
+  const int n_qt = (a.S + 32 * NW - 1) / (32 * NW);
+  dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
+  notify_launch("attn_fwd", 0, a.stream);
+  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB>), grid, block, 0, (hipStream_t)a.stream,
+                     (const typename E::T*)a.q, (const typename E::T*)a.k, (const typename E::T*)a.v,
+                     (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.causal, a.window,
+                     (float)((double)a.scale * 1.4426950408889634), n_qt);
+  notify_launch("attn_fwd", 1, a.stream);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_fwd(const Args& a) {
+  if (a.dtype == kBF16) return a.D == 64 ? launch_fwd_t<BF16, 64>(a) : launch_fwd_t<BF16, 128>(a);
+  return a.D == 64 ? launch_fwd_t<F32, 64>(a) : launch_fwd_t<F32, 128>(a);
+}
+
+}  // namespace fa

@@ -1,0 +1,249 @@
+// device.h -- gfx950 building blocks for the attention kernels: element types, the 32x32 MFMA
+// tile, the swizzled LDS tile layout and operand-fragment loads.
+//
+// MFMA 32x32 tile (v_mfma_f32_32x32x16_bf16; for f32, eight v_mfma_f32_32x32x2f32), lane l of the
+// 64-lane wave, h = l / 32:
+//   A operand: row m = l % 32, contraction elements k = 8h + e (e = 0..7, one 16-byte fragment)
+//   B operand: column n = l % 32, contraction elements k = 8h + e
+//   C/D accumulator register r (0..15): row 8*(r/4) + 4h + r%4, column l % 32
+// So a lane's accumulator holds 16 rows of one column. Feeding those 16 values back as the
+// contraction side of the next product needs no data movement: registers 8t..8t+7 cover rows
+// 16t + 8*(e/4) + 4h + e%4, and the other operand is fetched with the same row permutation
+// (tr_frag). The f32 variant feeds element e of every lane's fragment to the e-th 32x32x2 step,
+// which contracts the same index set.
+#ifndef ATTN_DEVICE_H_
+#define ATTN_DEVICE_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tiles.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct BF16 {
+  typedef uint16_t T;
+  static constexpr int kBytes = 2;
+};
+struct F32 {
+  typedef float T;
+  static constexpr int kBytes = 4;
+};
+
+// Eight consecutive contraction elements of one operand row/column.
+template <class E> struct Frag;
+template <> struct Frag<BF16> { u32x4_t v; };
+template <> struct Frag<F32> { f32x4_t lo, hi; };
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ void mma(f32x16_t& acc, const Frag<BF16>& a, const Frag<BF16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                __builtin_bit_cast(bf16x8_t, b.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16_t& acc, const Frag<F32>& a, const Frag<F32>& b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[e], b.lo[e], acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[e], b.hi[e], acc, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Accumulator registers 8t..8t+7 as a contraction fragment (rows 16t + 8*(e/4) + 4h + e%4).
+__device__ __forceinline__ Frag<BF16> acc_frag_bf16(const f32x16_t& a, int t) {
+  Frag<BF16> f;
+  f.v[0] = pack_bf16x2(a[8 * t + 0], a[8 * t + 1]);
+  f.v[1] = pack_bf16x2(a[8 * t + 2], a[8 * t + 3]);
+  f.v[2] = pack_bf16x2(a[8 * t + 4], a[8 * t + 5]);
+  f.v[3] = pack_bf16x2(a[8 * t + 6], a[8 * t + 7]);
+  return f;
+}
+template <class E> __device__ __forceinline__ Frag<E> acc_frag(const f32x16_t& a, int t);
+template <> __device__ __forceinline__ Frag<BF16> acc_frag<BF16>(const f32x16_t& a, int t) {
+  return acc_frag_bf16(a, t);
+}
+template <> __device__ __forceinline__ Frag<F32> acc_frag<F32>(const f32x16_t& a, int t) {
+  Frag<F32> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.lo[e] = a[8 * t + e];
+    f.hi[e] = a[8 * t + 4 + e];
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------- global fragments
+// 8 consecutive elements from global memory (16 B for bf16, 32 B for f32), or zeros.
+__device__ __forceinline__ Frag<BF16> load_frag_global(const uint16_t* p, bool ok) {
+  Frag<BF16> f;
+  f.v = ok ? *reinterpret_cast<const u32x4_t*>(p) : u32x4_t{0, 0, 0, 0};
+  return f;
+}
+__device__ __forceinline__ Frag<F32> load_frag_global(const float* p, bool ok) {
+  Frag<F32> f;
+  if (ok) {
+    f.lo = *reinterpret_cast<const f32x4_t*>(p);
+    f.hi = *reinterpret_cast<const f32x4_t*>(p + 4);
+  } else {
+    f.lo = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f.hi = f.lo;
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------- LDS tiles
+// A tile of ROWS rows x D elements, row-major, unpadded, stored as 16-byte chunks whose position
+// inside the row is XOR-swizzled by the row index. The swizzle makes both access patterns used
+// here free of bank conflicts: 16 lanes reading the same chunk of 16 consecutive rows (row_frag),
+// and the transposing 8-byte reads of 4 consecutive rows x 64 bytes (tr_frag).
+template <class E, int ROWS, int D>
+struct LdsTile {
+  static constexpr int kRowBytes = D * E::kBytes;
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kBytes = ROWS * kRowBytes;
+  static_assert(kChunks >= 8, "row must hold at least 8 chunks");
+
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (kChunks >= 16) return 4 * (row & 3) + ((row >> 2) & 3);
+    else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  }
+  __device__ static __forceinline__ int chunk_off(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+  }
+};
+
+template <class Tile>
+__device__ __forceinline__ void lds_store_chunk(char* base, int row, int chunk, u32x4_t v) {
+  *reinterpret_cast<u32x4_t*>(base + Tile::chunk_off(row, chunk)) = v;
+}
+template <class Tile>
+__device__ __forceinline__ u32x4_t lds_load_chunk(const char* base, int row, int chunk) {
+  return *reinterpret_cast<const u32x4_t*>(base + Tile::chunk_off(row, chunk));
+}
+
+// Fragment of row `row`, contraction elements 16s + 8h .. +7 (h = lane / 32).
+template <class E, class Tile> struct RowFrag;
+template <class Tile> struct RowFrag<BF16, Tile> {
+  __device__ static __forceinline__ Frag<BF16> get(const char* base, int row, int s) {
+    Frag<BF16> f;
+    f.v = lds_load_chunk<Tile>(base, row, 2 * s + (lane_id() >> 5));
+    return f;
+  }
+};
+template <class Tile> struct RowFrag<F32, Tile> {
+  __device__ static __forceinline__ Frag<F32> get(const char* base, int row, int s) {
+    Frag<F32> f;
+    int c = 4 * s + 2 * (lane_id() >> 5);
+    f.lo = __builtin_bit_cast(f32x4_t, lds_load_chunk<Tile>(base, row, c));
+    f.hi = __builtin_bit_cast(f32x4_t, lds_load_chunk<Tile>(base, row, c + 1));
+    return f;
+  }
+};
+
+// Transposed fragment: column n0 + lane % 32 of the tile, contraction over tile rows
+// kbase + 8*(e/4) + 4h + e%4 (e = 0..7), i.e. the permutation that matches acc_frag(..., t)
+// with kbase = 32*block + 16t. For bf16 this is two ds_read_b64_tr_b16: within each group of 16
+// lanes, lane s reads 4 elements at (row k0 + s/4, column c0 + 4*(s%4)) and receives column
+// c0 + s of rows k0 .. k0+3.
+template <class E, class Tile> struct TrFrag;
+template <class Tile> struct TrFrag<BF16, Tile> {
+  __device__ static __forceinline__ Frag<BF16> get(const char* base, int kbase, int n0) {
+    const int l = lane_id();
+    const int s = l & 15;
+    const int col = n0 + 16 * ((l >> 4) & 1) + 4 * (s & 3);
+    const int row = kbase + 4 * (l >> 5) + (s >> 2);
+    const int chunk = col >> 3;
+    const int sub = (s & 1) * 8;
+    const char* pa = base + Tile::chunk_off(row, chunk) + sub;
+    const char* pb = base + Tile::chunk_off(row + 8, chunk) + sub;
+    s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)((__attribute__((address_space(3))) char*)(pa)));
+    s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)((__attribute__((address_space(3))) char*)(pb)));
+    Frag<BF16> f;
+    u32x2_t ua = __builtin_bit_cast(u32x2_t, a);
+    u32x2_t ub = __builtin_bit_cast(u32x2_t, b);
+    f.v = u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+    return f;
+  }
+};
+template <class Tile> struct TrFrag<F32, Tile> {
+  __device__ static __forceinline__ Frag<F32> get(const char* base, int kbase, int n0) {
+    const int l = lane_id();
+    const int col = n0 + (l & 31);
+    const int rb = kbase + 4 * (l >> 5);
+    Frag<F32> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.lo[e] = *reinterpret_cast<const float*>(base + Tile::chunk_off(rb + e, col >> 2) + (col & 3) * 4);
+      f.hi[e] = *reinterpret_cast<const float*>(base + Tile::chunk_off(rb + 8 + e, col >> 2) + (col & 3) * 4);
+    }
+    return f;
+  }
+};
+
+// Cooperative copy of rows [row0, row0 + ROWS) of a [S, D] matrix into an LDS tile; rows at or
+// beyond S are written as zeros (so masked keys contribute exact zeros, never NaN).
+template <class E, class Tile, int ROWS, int D, int NTHREADS>
+__device__ __forceinline__ void load_tile(char* lds, const typename E::T* __restrict__ src, int row0, int S) {
+  constexpr int kChunksPerRow = Tile::kChunks;
+  constexpr int kTotal = ROWS * kChunksPerRow;
+  static_assert(kTotal % NTHREADS == 0, "tile chunks must divide evenly over the threads");
+  constexpr int kPer = kTotal / NTHREADS;
+  u32x4_t v[kPer];
+#pragma unroll
+  for (int n = 0; n < kPer; ++n) {
+    const int c = threadIdx.x + n * NTHREADS;
+    const int r = c / kChunksPerRow;
+    const int ch = c % kChunksPerRow;
+    const bool ok = row0 + r < S;
+    const char* p = reinterpret_cast<const char*>(src + (size_t)(row0 + r) * D) + ch * 16;
+    v[n] = ok ? *reinterpret_cast<const u32x4_t*>(p) : u32x4_t{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int n = 0; n < kPer; ++n) {
+    const int c = threadIdx.x + n * NTHREADS;
+    lds_store_chunk<Tile>(lds, c / kChunksPerRow, c % kChunksPerRow, v[n]);
+  }
+}
+
+// Max / sum of a value held by lanes l and l ^ 32 (the two halves of one accumulator column).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Accumulator row index (within a 32 x 32 tile) held in register r by this lane.
+__device__ __forceinline__ int acc_row(int r) { return 8 * (r >> 2) + 4 * (lane_id() >> 5) + (r & 3); }
+
+}  // namespace fa
+
+#endif  // ATTN_DEVICE_H_

@@ -1,0 +1,98 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) causal / sliding-window grouped-query attention library
+ * (libattn.so): a tiled forward that writes O and the per-row log-sum-exp, and a backward that
+ * takes dO and writes dQ, dK and dV.
+ *
+ * What the calls compute:
+ *   "KYNETRA FOUNDRY" page, FlashAttention paragraph: for each query tile the kernel streams key /
+ *   value tiles through on-chip memory with a running-max / running-sum softmax, never writing the
+ *   S x S score matrix to HBM; numerics are those of plain attention; the backward recomputes tiles.
+ *   Same page, Grip paragraph: query heads are partitioned into groups that share one K/V head.
+ *   Same page, decoder-block paragraph: the causal mask is strict left-to-right.
+ *   "CUDA-LLM: A GitHub Repository for Development", section "The custom CUDA kernel": one window
+ *   parameter switches between full-causal and sliding-window attention; the backward recomputes the
+ *   softmax probabilities from the saved log-sum-exp.
+ *
+ * Definitions (for b < B, query head h < Hq, KV head g = h / (Hq / Hkv), rows i, keys j < S):
+ *   visible(i, j) = (causal == 0 || j <= i) && (window == 0 || i - j < window)
+ *   x_ij   = scale * <Q[b,h,i,:], K[b,g,j,:]>            (visible j only)
+ *   lse_i  = ln( sum_j exp(x_ij) )                       (natural log of the scaled scores)
+ *   P_ij   = exp(x_ij - lse_i),  O_i = sum_j P_ij V[b,g,j,:]
+ *   dQ_i   = scale * sum_j dS_ij K_j,  dK_j = scale * sum_{h in group(g)} sum_i dS_ij Q_i,
+ *   dV_j   = sum_{h in group(g)} sum_i P_ij dO_i,  with dS_ij = P_ij (<dO_i, V_j> - <dO_i, O_i>).
+ *   A window W >= 1 lets query i see keys i-W+1 .. i (W counts the diagonal). W = 0: no window.
+ *
+ * Layout: Q, O, dO, dQ are [B, Hq, S, D]; K, V, dK, dV are [B, Hkv, S, D]; lse is [B, Hq, S]. All
+ * are dense and contiguous with D fastest, element type `dtype` (lse is always float32).
+ *
+ * Ownership and execution: every pointer is a DEVICE pointer owned by the caller. The library
+ * never allocates, never synchronises the host, keeps no per-call state, and enqueues all of its
+ * work on `stream` (a hipStream_t; NULL = the default stream). Outputs must not alias inputs.
+ * Calls on different streams may run concurrently; results are deterministic (no atomics).
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; a failed check returns a
+ * status and enqueues nothing. A launch failure reported by the HIP runtime returns
+ * ATTN_ERR_DEVICE. Faults during execution surface at the caller's next synchronisation.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,     /* null pointer, size <= 0, Hq % Hkv != 0, window < 0, non-finite
+                               scale, workspace too small */
+  ATTN_ERR_UNSUPPORTED = 2, /* D not 64 or 128, unknown dtype, window > 0 without causal,
+                               B*Hq*S*D >= 2^31 */
+  ATTN_ERR_DEVICE = 3       /* the HIP runtime reported an error for a launch */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Forward. Reads q [B,Hq,S,D], k and v [B,Hkv,S,D]; writes o [B,Hq,S,D] (dtype, fp32 accumulation
+ * rounded to nearest even) and lse [B,Hq,S] (float32, natural log). */
+int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int S, int D, int causal, int window, float scale,
+             void* stream);
+
+/* Bytes of device workspace attn_bwd needs for these sizes (per-row delta = rowsum(dO * O) and
+ * nothing else). Returns 0 for sizes attn_bwd would reject. */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
+
+/* Backward. o and lse must be exactly what attn_fwd wrote for the same q, k, v and arguments.
+ * dout [B,Hq,S,D] is the gradient of the loss with respect to o. Writes dq [B,Hq,S,D] and dk, dv
+ * [B,Hkv,S,D]; all three are fully overwritten (not accumulated into). `workspace` is a device
+ * buffer of at least attn_bwd_workspace_bytes(...) bytes; its contents on entry do not matter. */
+int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes,
+             int B, int Hq, int Hkv, int S, int D, int causal, int window, float scale,
+             void* stream);
+
+/* Optional launch observer, for profiling. When set, every entry point calls
+ * hook(kernel, 0, stream, user) just before and hook(kernel, 1, stream, user) just after it
+ * enqueues each of its kernels ("attn_fwd", "attn_bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq"),
+ * on the calling thread, so the hook can record timing events on `stream` around exactly one
+ * kernel. NULL (the default) turns it off. The setting is process-wide; set it while no other
+ * thread is calling the library. */
+typedef void (*attn_launch_hook_t)(const char* kernel, int after, void* stream, void* user);
+void attn_set_launch_hook(attn_launch_hook_t hook, void* user);
+
+/* Static, NUL-terminated description of a status code. */
+const char* attn_status_string(int status);
+
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

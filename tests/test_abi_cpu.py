@@ -1,0 +1,123 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/attn.h declares,
+and rejects invalid arguments on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+PKG = os.path.join(ROOT, "causal_attention_fa2_amd")
+
+import causal_attention_fa2_amd as fa  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from causal_attention_fa2_amd.build import build
+        build()
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd",
+                     "attn_set_launch_hook", "attn_status_string"]
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings(lib):
+    assert fa.attn_abi_version() == 1
+    assert fa.attn_status_string(0) == "ok"
+    assert fa.attn_status_string(1) == "invalid argument"
+    assert fa.attn_status_string(2) == "unsupported configuration"
+    assert fa.attn_status_string(3) == "HIP runtime error at launch"
+    assert fa.attn_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert fa.attn_bwd_workspace_bytes(1, 64, 8, 4096, 128) == 64 * 4096 * 4
+    assert fa.attn_bwd_workspace_bytes(1, 2, 2, 3, 64) == 256  # rounded up to 256 bytes
+    assert fa.attn_bwd_workspace_bytes(1, 3, 2, 64, 64) == 0   # Hq % Hkv != 0
+    assert fa.attn_bwd_workspace_bytes(1, 2, 2, 64, 96) == 0   # unsupported D
+
+
+P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def fwd(lib, dtype=1, ptrs=(P, P, P, P, P), B=1, Hq=2, Hkv=2, S=64, D=64, causal=1, window=0,
+        scale=0.125):
+    return lib.attn_fwd(dtype, *ptrs, B, Hq, Hkv, S, D, causal, window, scale, None)
+
+
+def bwd(lib, ws_bytes=0, ptrs=(P,) * 10, B=1, Hq=2, Hkv=2, S=64, D=64, causal=1, window=0,
+        scale=0.125, dtype=1):
+    return lib.attn_bwd(dtype, *ptrs, ws_bytes, B, Hq, Hkv, S, D, causal, window, scale, None)
+
+
+def test_fwd_validation(lib):
+    INV, UNS = fa.ATTN_ERR_INVALID, fa.ATTN_ERR_UNSUPPORTED
+    for i in range(5):
+        ptrs = [P] * 5
+        ptrs[i] = None
+        assert fwd(lib, ptrs=ptrs) == INV
+    assert fwd(lib, B=0) == INV
+    assert fwd(lib, S=-1) == INV
+    assert fwd(lib, Hq=3, Hkv=2) == INV
+    assert fwd(lib, window=-1) == INV
+    assert fwd(lib, scale=float("nan")) == INV
+    assert fwd(lib, scale=float("inf")) == INV
+    assert fwd(lib, causal=2) == INV
+    assert fwd(lib, D=96) == UNS
+    assert fwd(lib, dtype=7) == UNS
+    assert fwd(lib, causal=0, window=4) == UNS
+    assert fwd(lib, B=1, Hq=64, Hkv=8, S=262144, D=128) == UNS  # 2^31 elements
+
+
+def test_bwd_validation(lib):
+    INV, UNS = fa.ATTN_ERR_INVALID, fa.ATTN_ERR_UNSUPPORTED
+    need = fa.attn_bwd_workspace_bytes(1, 2, 2, 64, 64)
+    for i in range(10):
+        ptrs = [P] * 10
+        ptrs[i] = None
+        assert bwd(lib, need, ptrs=ptrs) == INV
+    assert bwd(lib, need - 1) == INV
+    assert bwd(lib, need, Hq=4, Hkv=3) == INV
+    assert bwd(lib, need, D=32) == UNS
+    assert bwd(lib, need, causal=0, window=1) == UNS
+
+
+def test_launch_hook_set_and_clear(lib):
+    seen = []
+    fa.attn_set_launch_hook(lambda k, a, s: seen.append((k, a)))
+    assert fwd(lib, D=96) == fa.ATTN_ERR_UNSUPPORTED  # rejected calls enqueue nothing
+    assert seen == []
+    fa.attn_set_launch_hook(None)
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(RuntimeError):
+        fa.load_library(str(tmp_path / "nope.so"))
+
+
+def test_product_never_touches_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
+                assert "oracle." not in text, f
