@@ -31,6 +31,7 @@ KERNEL_SOURCES = {
     "attn_bwd_delta": ["attn_bwd.hip", "device.h"],
     "attn_bwd_dkdv": ["attn_bwd.hip", "device.h", "tiles.h"],
     "attn_bwd_dq": ["attn_bwd.hip", "device.h", "tiles.h"],
+    "attn_bwd_dkdv_reduce": ["attn_bwd.hip", "device.h"],
 }
 
 
@@ -94,7 +95,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa64x8-s4096-d128")
-    ap.add_argument("--cpu-heads", type=int, default=24,
+    ap.add_argument("--cpu-heads", type=int, default=64,
                     help="query heads in the CPU oracle sample (rounded to whole KV groups)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -165,6 +166,11 @@ def main() -> int:
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     eb = 2 if w.dtype == "bf16" else 4
     delta_bytes = w.B * w.Hq * w.S * (2 * w.D * eb + 4)
+    nkv = w.B * w.Hkv * w.S * w.D
+    ws_bytes = fa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D)
+    parts = (ws_bytes - ((w.B * w.Hq * w.S * 4 + 255) // 256 * 256)) // (2 * nkv * 4)
+    hbm_bytes = {"attn_bwd_delta": delta_bytes,
+                 "attn_bwd_dkdv_reduce": 2 * nkv * (4 * max(parts, 1) + eb)}
 
     kernels = {}
     for name, t in kern_ms.items():
@@ -172,7 +178,7 @@ def main() -> int:
         if name in fl:
             rec["tflops"] = round(fl[name] / (t * 1e-3) / 1e12, 1)
         else:
-            rec["gbs"] = round(delta_bytes / (t * 1e-3) / 1e9, 1)
+            rec["gbs"] = round(hbm_bytes[name] / (t * 1e-3) / 1e9, 1)
         kernels[name] = rec
     dom = max(kern_ms, key=kern_ms.get)
     if dom in fl:
@@ -180,7 +186,7 @@ def main() -> int:
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     else:
-        ach = delta_bytes / (kern_ms[dom] * 1e-3) / 1e9
+        ach = hbm_bytes[dom] / (kern_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
     roof["traffic"] = load_traffic(dom, w.name)

@@ -77,7 +77,7 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
   if (check_common(ATTN_BF16, B, Hq, Hkv, S, D, 1, 0, 1.0f) != ATTN_OK) return 0;
-  return fa::bwd_workspace_bytes(B, Hq, S);
+  return fa::bwd_workspace_bytes(B, Hq, Hkv, S, D);
 }
 
 int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
@@ -88,7 +88,7 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
     return ATTN_ERR_INVALID;
   int st = check_common(dtype, B, Hq, Hkv, S, D, causal, window, scale);
   if (st != ATTN_OK) return st;
-  if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, S)) return ATTN_ERR_INVALID;
+  if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, Hkv, S, D)) return ATTN_ERR_INVALID;
   fa::Args a{};
   a.dtype = dtype;
   a.q = q;
@@ -101,6 +101,7 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
   a.dk = dk;
   a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::delta_bytes(B, Hq, S));
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

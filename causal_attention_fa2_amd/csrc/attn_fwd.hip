@@ -10,11 +10,16 @@
 //   * each wave owns 32 query rows; its Q rows stay in registers for the whole kernel as the
 //     B operand of S^T = K Q^T (one accumulator column per query, so every lane owns one query:
 //     the row max / row sum are in-lane plus one permlane32 swap with the partner lane);
-//   * key / value tiles of 32*KB rows are copied into swizzled LDS tiles shared by the waves;
+//   * key / value tiles of 32*KB rows stream through a 3-stage ring of swizzled LDS tiles filled
+//     by LDS-DMA (global_load_lds_dwordx4): the copy of tile s+1 is in flight while tile s is
+//     used, with one workgroup barrier per tile;
 //   * P^T stays in registers and is the B operand of O^T = V^T P^T; V^T comes from LDS with the
 //     gfx950 transposing read, so V is never transposed in memory;
 //   * key tiles outside a wave's causal / window band are skipped, only boundary tiles are masked;
 //   * softmax runs in base 2 (scale * log2 e folded into one multiply); lse is exported as ln.
+//   * grid order: heaviest query tiles first; within one tile index the query heads of a KV group
+//     are consecutive multiples of B*Hkv apart, so with round-robin XCD dispatch a KV group's
+//     workgroups share one XCD (and its L2) when B*Hkv is a multiple of 8.
 #include "device.h"
 #include "launch.h"
 
@@ -30,32 +35,47 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   constexpr int DS = D / 16;  // 16-wide contraction steps over the head dimension
   constexpr int DB = D / 32;  // 32-wide output blocks over the head dimension
   typedef LdsTile<E, BC, D> KvTile;
-  __shared__ __attribute__((aligned(16))) char smem[2 * KvTile::kBytes];
-  char* k_lds = smem;
-  char* v_lds = smem + KvTile::kBytes;
+  constexpr int kStage = 2 * KvTile::kBytes;
+  constexpr int kOps = 2 * dma_tile_ops<E, BC, D, NW>();  // DMA instructions per wave per stage
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kStage];
 
   const int lane = lane_id();
-  const int w = threadIdx.x >> 6;
+  const int w = wave_id();
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // Heaviest query tiles first (causal work grows with the tile index); heads vary fastest.
-  const int BH = B * Hq;
-  const int rank = blockIdx.x / BH;
-  const int bh = blockIdx.x - rank * BH;
+  const int G = Hq / Hkv;
+  const int BG = B * Hkv;
+  const int bg = blockIdx.x % BG;
+  const int rest = blockIdx.x / BG;
+  const int hh = rest % G;
+  const int rank = rest / G;
   const int qt = causal ? n_qt - 1 - rank : rank;
-  const int b = bh / Hq;
-  const int h = bh - b * Hq;
-  const int g = h / (Hq / Hkv);
+  const int b = bg / Hkv;
+  const int g = bg - b * Hkv;
+  const int h = g * G + hh;
 
   const typename E::T* q_bh = Q + (size_t)(b * Hq + h) * S * D;
-  const typename E::T* k_bg = K + (size_t)(b * Hkv + g) * S * D;
-  const typename E::T* v_bg = V + (size_t)(b * Hkv + g) * S * D;
+  const typename E::T* k_bg = K + (size_t)bg * S * D;
+  const typename E::T* v_bg = V + (size_t)bg * S * D;
 
   const int q0 = qt * BR;
   const int qw = q0 + 32 * w;  // first row of this wave
   const int my_q = qw + l32;   // the query row this lane owns
   const bool q_ok = my_q < S;
+
+  int jt_lo, jt_hi;
+  kv_tile_range(q0, imin_(q0 + BR - 1, S - 1), S, BC, causal, window, &jt_lo, &jt_hi);
+  const int n_steps = jt_hi - jt_lo + 1;
+
+  auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
+    const int j0 = (jt_lo + s) * BC;
+    dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
+    dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
+  };
+  issue(0, st0);
 
   Frag<E> qf[DS];
 #pragma unroll
@@ -64,19 +84,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   f32x16_t acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+  wait_vmcnt<0>();  // Q fragments and the first tile have landed; the loop tracks only its own copies
   float m = kNegInf;  // running max of base-2 scores
   float l = 0.f;      // running sum of exp2(score - m)
 
-  int jt_lo, jt_hi;
-  kv_tile_range(q0, imin_(q0 + BR - 1, S - 1), S, BC, causal, window, &jt_lo, &jt_hi);
-
-  for (int jt = jt_lo; jt <= jt_hi; ++jt) {
-    const int j0 = jt * BC;
-    __syncthreads();
-    load_tile<E, KvTile, BC, D, NW * 64>(k_lds, k_bg, j0, S);
-    load_tile<E, KvTile, BC, D, NW * 64>(v_lds, v_bg, j0, S);
-    __syncthreads();
-    if (block_empty(qw, qw + 31, j0, j0 + BC - 1, S, causal, window)) continue;
+  auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
+    const char* v_lds = k_lds + KvTile::kBytes;
+    const int j0 = (jt_lo + s) * BC;
+    if (block_empty(qw, qw + 31, j0, j0 + BC - 1, S, causal, window)) return;
     const bool full = block_full(qw, qw + 31, j0, j0 + BC - 1, S, causal, window);
 
     // S^T = K Q^T for KB blocks of 32 keys: lane owns query my_q, registers hold keys.
@@ -85,23 +100,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     for (int kb = 0; kb < KB; ++kb) {
       st[kb] = f32x16_t{};
 #pragma unroll
-      for (int s = 0; s < DS; ++s) mma(st[kb], RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s), qf[s]);
+      for (int s2 = 0; s2 < DS; ++s2) mma(st[kb], RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s2), qf[s2]);
     }
 
     float tmax = kNegInf;
+    auto scale_mask = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = st[kb][r] * scale_log2;
-        if (!full) {
-          const int j = j0 + 32 * kb + acc_row(r);
-          if (!visible(my_q, j, S, causal, window)) x = kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          float x = st[kb][r] * scale_log2;
+          if constexpr (decltype(maskc)::value) {
+            if (!visible(my_q, j0 + 32 * kb + acc_row(r), S, causal, window)) x = kNegInf;
+          }
+          st[kb][r] = x;
+          tmax = fmaxf(tmax, x);
         }
-        st[kb][r] = x;
-        tmax = fmaxf(tmax, x);
       }
-    }
+    };
+    if (full) scale_mask(IC<0>{});
+    else scale_mask(IC<1>{});
     tmax = pair_max(tmax);
     const float m_new = fmaxf(m, tmax);
     const float m_use = m_new == kNegInf ? 0.f : m_new;  // row with nothing visible yet
@@ -133,6 +151,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
           mma(acc[db], TrFrag<E, KvTile>::get(v_lds, 32 * kb + 16 * t, 32 * db), pf);
       }
     }
+  };
+
+  // One step: start the copy of tile s+1, wait for this wave's part of tile s, barrier, use s.
+  auto step = [&](auto stc, int s) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stc)::value;
+    char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
+    char* nxt = ST == 0 ? st1 : (ST == 1 ? st2 : st0);
+    if (s + 1 < n_steps) {
+      issue(s + 1, nxt);
+      wait_vmcnt<kOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_keep_vm();
+    compute(s, cur);
+  };
+  for (int s = 0; s < n_steps; s += 3) {
+    step(IC<0>{}, s);
+    if (s + 1 < n_steps) step(IC<1>{}, s + 1);
+    if (s + 2 < n_steps) step(IC<2>{}, s + 2);
   }
 
   if (!q_ok) return;
@@ -157,7 +195,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 
 template <class E, int D>
 static int launch_fwd_t(const Args& a) {
-  constexpr int NW = 4, KB = 2;
+  constexpr int NW = E::kBytes == 2 ? 8 : 4;
+  constexpr int KB = E::kBytes == 2 ? 2 : 1;
   const int n_qt = (a.S + 32 * NW - 1) / (32 * NW);
   dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
   notify_launch("attn_fwd", 0, a.stream);

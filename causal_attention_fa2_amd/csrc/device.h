@@ -28,6 +28,9 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -68,8 +71,9 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// Two floats -> packed bfloat16 pair (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -239,6 +243,81 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int N> struct IC { static constexpr int value = N; };  // compile-time stage index
+
+// ---------------------------------------------------------------- asynchronous tile copies
+// Wave index as a scalar (it is uniform across the wave; LDS-DMA needs the LDS address in M0).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 s_waitcnt
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that waits for this wave's own LDS instructions (lgkmcnt 0) but not for its
+// outstanding vector-memory traffic, so LDS-DMA copies of later stages stay in flight. The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_vm() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+// LDS-DMA: each lane copies 16 (resp. 4) bytes from its global address to LDS at
+// lds_base + 16 * lane (resp. 4 * lane); lds_base must be wave-uniform (it goes to M0). Issued
+// through inline asm so that the compiler does not add its own conservative wait for these copies
+// before LDS reads: the kernels order them explicitly with wait_vmcnt<> + barrier_keep_vm().
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"((uint64_t)(uintptr_t)gptr), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"((uint64_t)(uintptr_t)gptr), "s"(lds_base) : "memory", "m0");
+}
+
+// Issue this wave's share of an asynchronous copy of rows [row0, row0 + ROWS) of a row-major
+// [S, D] matrix into a swizzled LDS tile. One 16-byte LDS-DMA per lane moves 1 KB per wave:
+// lane l writes the 16 bytes at (block base + 16 l), so lane l fetches the global chunk the
+// swizzle puts there. Rows at or past S are read from row S - 1: finite data whose scores /
+// products the masks zero. NW waves share the work; the caller waits with wait_vmcnt<>.
+template <class E, int ROWS, int D, int NW>
+__device__ __forceinline__ void dma_tile(char* lds, const typename E::T* __restrict__ src, int row0, int S) {
+  typedef LdsTile<E, ROWS, D> Tile;
+  constexpr int kBlocks = Tile::kBytes / 1024;
+  static_assert(kBlocks % NW == 0, "tile must split into whole 1 KB blocks per wave");
+  const int lane = lane_id();
+  const int w = wave_id();
+  const uint32_t base = lds_addr(lds);
+#pragma unroll
+  for (int n = 0; n < kBlocks / NW; ++n) {
+    const int blk = n * NW + w;
+    const int c = blk * 64 + lane;
+    const int r = c / Tile::kChunks;
+    const int pos = c % Tile::kChunks;
+    const int gr = imin_(row0 + r, S - 1);
+    const char* g = reinterpret_cast<const char*>(src + (size_t)gr * D) + ((pos ^ Tile::swz(r)) << 4);
+    dma16(g, base + blk * 1024);
+  }
+}
+template <class E, int ROWS, int D, int NW>
+constexpr int dma_tile_ops() { return LdsTile<E, ROWS, D>::kBytes / 1024 / NW; }
+
+// 64 consecutive floats src[clamp(i0 + lane)] -> lds[0..63] (one wave, one instruction).
+__device__ __forceinline__ void dma_row_floats(char* lds, const float* __restrict__ src, int i0, int S) {
+  const int r = imin_(i0 + lane_id(), S - 1);
+  dma4(src + r, lds_addr(lds));
 }
 
 // Accumulator row index (within a 32 x 32 tile) held in register r by this lane.

@@ -21,6 +21,7 @@ struct Args {
   void* dk;
   void* dv;
   float* delta;       // backward workspace: rowsum(dO * O), [B, Hq, S]
+  float* part;        // backward workspace: fp32 dK / dV partial sums of the head-group parts
   int B, Hq, Hkv, S, D;
   int causal, window;
   float scale;
@@ -35,9 +36,33 @@ void notify_launch(const char* kernel, int after, void* stream);
 int launch_fwd(const Args& a);
 int launch_bwd(const Args& a);
 
-inline size_t bwd_workspace_bytes(int B, int Hq, int S) {
-  size_t delta = (size_t)B * Hq * S * sizeof(float);
-  return (delta + 255) / 256 * 256;
+// dK/dV decomposition: a workgroup of kDkdvWaves waves owns 32*kDkdvWaves keys and processes key
+// tile j and then key tile n_kt-1-j (equal work per workgroup under the causal mask). When that
+// gives fewer than kDkdvMinGroups workgroups, the query-head group is split into `hs` parts (a
+// power of two dividing Hq/Hkv) whose fp32 partial sums are reduced by a second kernel.
+constexpr int kDkdvWaves = 4;
+constexpr int kDkdvMinGroups = 256;
+struct DkdvPlan {
+  int n_kt, n_pairs, hs;
+};
+inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int S) {
+  DkdvPlan p;
+  p.n_kt = (S + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
+  p.n_pairs = (p.n_kt + 1) / 2;
+  const long items = (long)B * Hkv * p.n_pairs;
+  const int G = Hq / Hkv;
+  p.hs = 1;
+  while (items * p.hs < kDkdvMinGroups && G % (2 * p.hs) == 0) p.hs *= 2;
+  return p;
+}
+
+inline size_t delta_bytes(int B, int Hq, int S) {
+  return ((size_t)B * Hq * S * sizeof(float) + 255) / 256 * 256;
+}
+inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
+  const DkdvPlan p = dkdv_plan(B, Hq, Hkv, S);
+  size_t partials = p.hs > 1 ? (size_t)p.hs * 2 * B * Hkv * S * D * sizeof(float) : 0;
+  return delta_bytes(B, Hq, S) + partials;
 }
 
 }  // namespace fa

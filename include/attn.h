@@ -62,8 +62,9 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
              int B, int Hq, int Hkv, int S, int D, int causal, int window, float scale,
              void* stream);
 
-/* Bytes of device workspace attn_bwd needs for these sizes (per-row delta = rowsum(dO * O) and
- * nothing else). Returns 0 for sizes attn_bwd would reject. */
+/* Bytes of device workspace attn_bwd needs for these sizes: the per-row delta = rowsum(dO * O)
+ * (B*Hq*S fp32) and, when the dK/dV pass splits a query-head group across workgroups, fp32 partial
+ * sums of dK and dV (2 * parts * B*Hkv*S*D fp32). Returns 0 for sizes attn_bwd would reject. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 
 /* Backward. o and lse must be exactly what attn_fwd wrote for the same q, k, v and arguments.
@@ -78,7 +79,8 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
 
 /* Optional launch observer, for profiling. When set, every entry point calls
  * hook(kernel, 0, stream, user) just before and hook(kernel, 1, stream, user) just after it
- * enqueues each of its kernels ("attn_fwd", "attn_bwd_delta", "attn_bwd_dkdv", "attn_bwd_dq"),
+ * enqueues each of its kernels ("attn_fwd", "attn_bwd_delta", "attn_bwd_dkdv",
+ * "attn_bwd_dkdv_reduce" (only when the head group is split), "attn_bwd_dq"),
  * on the calling thread, so the hook can record timing events on `stream` around exactly one
  * kernel. NULL (the default) turns it off. The setting is process-wide; set it while no other
  * thread is calling the library. */

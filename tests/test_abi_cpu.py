@@ -49,8 +49,25 @@ def test_version_and_status_strings(lib):
     assert fa.attn_status_string(99) == "unknown status"
 
 
+def _parts(B, Hq, Hkv, S):
+    """Head-group split of the dK/dV pass: key tiles of 128 paired, >= 256 workgroups wanted."""
+    pairs = (-(-S // 128) + 1) // 2
+    hs, G = 1, Hq // Hkv
+    while B * Hkv * pairs * hs < 256 and G % (2 * hs) == 0:
+        hs *= 2
+    return hs
+
+
 def test_workspace_bytes(lib):
-    assert fa.attn_bwd_workspace_bytes(1, 64, 8, 4096, 128) == 64 * 4096 * 4
+    for shp in ((1, 64, 8, 4096, 128), (4, 16, 16, 1024, 64), (1, 16, 16, 8192, 64),
+                (1, 64, 8, 32768, 128), (1, 4, 2, 300, 64), (1, 2, 2, 64, 64)):
+        B, Hq, Hkv, S, D = shp
+        hs = _parts(B, Hq, Hkv, S)
+        delta = (B * Hq * S * 4 + 255) // 256 * 256
+        part = 2 * hs * B * Hkv * S * D * 4 if hs > 1 else 0
+        assert fa.attn_bwd_workspace_bytes(*shp) == delta + part, shp
+    assert _parts(1, 64, 8, 4096) == 2 and _parts(1, 64, 8, 32768) == 1
+    assert fa.attn_bwd_workspace_bytes(1, 64, 8, 4096, 128) == 64 * 4096 * 4 + 2 * 2 * 8 * 4096 * 128 * 4
     assert fa.attn_bwd_workspace_bytes(1, 2, 2, 3, 64) == 256  # rounded up to 256 bytes
     assert fa.attn_bwd_workspace_bytes(1, 3, 2, 64, 64) == 0   # Hq % Hkv != 0
     assert fa.attn_bwd_workspace_bytes(1, 2, 2, 64, 96) == 0   # unsupported D
