@@ -98,6 +98,9 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="query heads in the CPU oracle sample (rounded to whole KV groups)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 elementwise copies of MIB MiB (reads MIB, writes MIB): the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -110,6 +113,16 @@ def main() -> int:
 
     import causal_attention_fa2_amd as fa
     from causal_attention_fa2_amd.workloads import WORKLOADS, make_inputs
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
+        return 0
 
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
@@ -165,10 +178,10 @@ def main() -> int:
     value = total_flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     eb = 2 if w.dtype == "bf16" else 4
-    delta_bytes = w.B * w.Hq * w.S * (2 * w.D * eb + 4)
+    delta_bytes = w.B * w.Hq * w.S * (2 * w.D * eb + 12)  # read O, dO, lse; write delta, lse2
     nkv = w.B * w.Hkv * w.S * w.D
     ws_bytes = fa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D)
-    parts = (ws_bytes - ((w.B * w.Hq * w.S * 4 + 255) // 256 * 256)) // (2 * nkv * 4)
+    parts = (ws_bytes - 2 * ((w.B * w.Hq * w.S * 4 + 255) // 256 * 256)) // (2 * nkv * 4)
     hbm_bytes = {"attn_bwd_delta": delta_bytes,
                  "attn_bwd_dkdv_reduce": 2 * nkv * (4 * max(parts, 1) + eb)}
 

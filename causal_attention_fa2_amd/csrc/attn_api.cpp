@@ -100,8 +100,10 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  const size_t row_bytes = fa::delta_bytes(B, Hq, S);
   a.delta = static_cast<float*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::delta_bytes(B, Hq, S));
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + row_bytes);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_bytes);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

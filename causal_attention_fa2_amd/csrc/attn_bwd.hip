@@ -6,11 +6,13 @@
 // the first page (dK and dV of a shared K/V head sum over its query-head group).
 //
 // Launches on the caller's stream, no atomics anywhere:
-//   1. delta_kernel: delta_i = sum_d dO_id * O_id in fp32 (O as the forward stored it).
+//   1. delta_kernel: delta_i = sum_d dO_id * O_id in fp32 (O as the forward stored it), and the
+//      base-2 log-sum-exp lse_i * log2(e) that the gradient kernels exponentiate against.
 //   2. dkdv_kernel: each wave owns 32 keys whose K and V rows stay in registers as B operands of
 //      S = Q K^T and dP = dO V^T, so a lane owns one key and its accumulator holds query rows --
 //      exactly the contraction side that dV += P^T dO and dK += dS^T Q need. Query / dO / lse /
-//      delta tiles of the group's heads stream through a 3-stage LDS-DMA ring; dK and dV for the
+//      delta tiles of the group's heads stream through a 3-stage LDS-DMA ring (two tiles in
+//      flight ahead of the one in use); dK and dV for the
 //      group accumulate in registers. A workgroup takes key tile j and then key tile T-1-j, so
 //      under the causal mask every workgroup does the same amount of work. When that leaves too
 //      few workgroups to fill the GPU, the head group is split into `hs` parts whose fp32 partial
@@ -28,7 +30,9 @@ namespace fa {
 template <class E, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const typename E::T* __restrict__ O,
                                                     const typename E::T* __restrict__ dO,
-                                                    float* __restrict__ delta, int rows) {
+                                                    const float* __restrict__ LSE,
+                                                    float* __restrict__ delta,
+                                                    float* __restrict__ lse2, int rows) {
   constexpr int TPR = D / 8;       // threads per row, 8 elements each
   constexpr int RPB = 256 / TPR;   // rows per block
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
@@ -51,14 +55,17 @@ __global__ __launch_bounds__(256) void delta_kernel(const typename E::T* __restr
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (part == 0 && row < rows) delta[row] = s;
+  if (part == 0 && row < rows) {
+    delta[row] = s;
+    lse2[row] = LSE[row] * kLog2e;  // base-2 log-sum-exp used by both gradient kernels
+  }
 }
 
 template <class E, int D, int NW, int QB>
 __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ delta, typename E::T* __restrict__ dK,
+    const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dK,
     typename E::T* __restrict__ dV, float* __restrict__ part, int B, int Hq, int Hkv, int S,
     int causal, int window, float scale, float scale_log2, int n_kt, int n_pairs, int hs) {
   constexpr int BC = 32 * NW;  // keys per workgroup
@@ -106,13 +113,15 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     n_steps = hpg * nq;
   };
   // step -> (query head, first query row) of the current segment
+  // Query tiles are visited from the last one down, so the workgroups of one KV head (which all
+  // end at the last query tile) sweep the same Q / dO tiles at about the same time.
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
     const int h = h0 + s / nq;
-    const int i0 = (lo + s % nq) * BR;
+    const int i0 = (lo + nq - 1 - s % nq) * BR;
     const size_t bh = (size_t)b * Hq + h;
     dma_tile<E, BR, D, NW>(stg, Q + bh * S * D, i0, S);
     dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * S * D, i0, S);
-    if (w == 0) dma_row_floats(stg + kRowOff, LSE + bh * S, i0, S);
+    if (w == 0) dma_row_floats(stg + kRowOff, LSE2 + bh * S, i0, S);
     if (w == 1) dma_row_floats(stg + kRowOff + 256, delta + bh * S, i0, S);
   };
 
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     const char* do_lds = q_lds + QTile::kBytes;
     const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
     const float* dl_lds = lse_lds + 64;
-    const int i0 = (lo + s % nq) * BR;
+    const int i0 = (lo + nq - 1 - s % nq) * BR;
     const int kw = kt * BC + 32 * w;
     const int my_k = kw + l32;
 #pragma unroll
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * r4 + c;
-            float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse4[c] * kLog2e));
+            float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse4[c]));
             if constexpr (decltype(maskc)::value) {
               if (!visible(i0 + rb + c, my_k, S, causal, window)) p = 0.f;
             }
@@ -211,15 +220,15 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   auto step = [&](auto stc, int s) __attribute__((always_inline)) {
     constexpr int ST = decltype(stc)::value;
     char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
-    char* nxt = ST == 0 ? st1 : (ST == 1 ? st2 : st0);
+    char* nn = ST == 0 ? st2 : (ST == 1 ? st0 : st1);
     if (s + 1 < n_steps) {
-      issue(s + 1, nxt);
       if (w < 2) wait_vmcnt<2 * kTileOps + 1>();
       else wait_vmcnt<2 * kTileOps>();
     } else {
       wait_vmcnt<0>();
     }
     barrier_keep_vm();
+    if (s + 2 < n_steps) issue(s + 2, nn);
     compute(s, cur);
   };
   const int n_seg = two ? 2 : 1;
@@ -228,6 +237,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     set_segment(seg ? tb : ta);
     load_kv();
     issue(0, st0);
+    if (n_steps > 1) issue(1, st1);
     wait_vmcnt<0>();
     for (int s = 0; s < n_steps; s += 3) {
       step(IC<0>{}, s);
@@ -266,7 +276,7 @@ template <class E, int D, int NW, int KB>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ delta, typename E::T* __restrict__ dQ,
+    const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dQ,
     int B, int Hq, int Hkv, int S, int causal, int window, float scale, float scale_log2, int n_qt) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 32 * KB;
@@ -312,6 +322,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
   };
   issue(0, st0);
+  if (n_steps > 1) issue(1, st1);
 
   Frag<E> qf[DS], df[DS];
 #pragma unroll
@@ -320,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     df[s] = load_frag_global(dO + q_off + (size_t)my_q * D + 16 * s + 8 * half, q_ok);
   }
   const size_t row_idx = (size_t)(b * Hq + h) * S + (q_ok ? my_q : 0);
-  const float nlse2 = -LSE[row_idx] * kLog2e;
+  const float nlse2 = -LSE2[row_idx];
   const float dl = delta[row_idx];
   f32x16_t acc[DB];
 #pragma unroll
@@ -364,14 +375,11 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   auto step = [&](auto stc, int s) __attribute__((always_inline)) {
     constexpr int ST = decltype(stc)::value;
     char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
-    char* nxt = ST == 0 ? st1 : (ST == 1 ? st2 : st0);
-    if (s + 1 < n_steps) {
-      issue(s + 1, nxt);
-      wait_vmcnt<kOps>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    char* nn = ST == 0 ? st2 : (ST == 1 ? st0 : st1);
+    if (s + 1 < n_steps) wait_vmcnt<kOps>();
+    else wait_vmcnt<0>();
     barrier_keep_vm();
+    if (s + 2 < n_steps) issue(s + 2, nn);
     compute(s, cur);
   };
   for (int s = 0; s < n_steps; s += 3) {
@@ -409,7 +417,7 @@ static int launch_bwd_t(const Args& a) {
     dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
     notify_launch("attn_bwd_delta", 0, a.stream);
     hipLaunchKernelGGL((delta_kernel<E, D>), grid, block, 0, st, (const T*)a.o_in, (const T*)a.dout,
-                       a.delta, rows);
+                       (const float*)a.lse, a.delta, a.lse2, rows);
     notify_launch("attn_bwd_delta", 1, a.stream);
   }
   {
@@ -419,7 +427,7 @@ static int launch_bwd_t(const Args& a) {
     dim3 grid((unsigned)(p.n_pairs * a.B * a.Hkv * p.hs)), block(NW * 64);
     notify_launch("attn_bwd_dkdv", 0, a.stream);
     hipLaunchKernelGGL((dkdv_kernel<E, D, NW, QB>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (const T*)a.dout, (const float*)a.lse, (const float*)a.delta,
+                       (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
                        (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.S, a.causal, a.window, a.scale,
                        scale_log2, p.n_kt, p.n_pairs, p.hs);
     notify_launch("attn_bwd_dkdv", 1, a.stream);
@@ -439,7 +447,7 @@ static int launch_bwd_t(const Args& a) {
     dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
     notify_launch("attn_bwd_dq", 0, a.stream);
     hipLaunchKernelGGL((dq_kernel<E, D, NW, KB>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (const T*)a.dout, (const float*)a.lse, (const float*)a.delta,
+                       (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
                        (T*)a.dq, a.B, a.Hq, a.Hkv, a.S, a.causal, a.window, a.scale, scale_log2, n_qt);
     notify_launch("attn_bwd_dq", 1, a.stream);
   }

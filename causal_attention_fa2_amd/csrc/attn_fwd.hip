@@ -11,12 +11,13 @@
 //     B operand of S^T = K Q^T (one accumulator column per query, so every lane owns one query:
 //     the row max / row sum are in-lane plus one permlane32 swap with the partner lane);
 //   * key / value tiles of 32*KB rows stream through a 3-stage ring of swizzled LDS tiles filled
-//     by LDS-DMA (global_load_lds_dwordx4): the copy of tile s+1 is in flight while tile s is
-//     used, with one workgroup barrier per tile;
+//     by LDS-DMA (global_load_lds_dwordx4): the copies of tiles s+1 and s+2 are in flight while
+//     tile s is used, with one workgroup barrier per tile;
 //   * P^T stays in registers and is the B operand of O^T = V^T P^T; V^T comes from LDS with the
 //     gfx950 transposing read, so V is never transposed in memory;
 //   * key tiles outside a wave's causal / window band are skipped, only boundary tiles are masked;
-//   * softmax runs in base 2 (scale * log2 e folded into one multiply); lse is exported as ln.
+//   * softmax runs in base 2 (scale * log2 e folded into one FMA per score); the O accumulator
+//     is rescaled only when a row max grows by more than 2^8; lse is exported as ln.
 //   * grid order: heaviest query tiles first; within one tile index the query heads of a KV group
 //     are consecutive multiples of B*Hkv apart, so with round-robin XCD dispatch a KV group's
 //     workgroups share one XCD (and its L2) when B*Hkv is a multiple of 8.
@@ -76,6 +77,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
   };
   issue(0, st0);
+  if (n_steps > 1) issue(1, st1);
 
   Frag<E> qf[DS];
 #pragma unroll
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   f32x16_t acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
-  wait_vmcnt<0>();  // Q fragments and the first tile have landed; the loop tracks only its own copies
+  wait_vmcnt<0>();  // Q fragments (and the first tiles) have landed before the loop
   float m = kNegInf;  // running max of base-2 scores
   float l = 0.f;      // running sum of exp2(score - m)
 
@@ -103,68 +105,71 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
       for (int s2 = 0; s2 < DS; ++s2) mma(st[kb], RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s2), qf[s2]);
     }
 
-    float tmax = kNegInf;
-    auto scale_mask = [&](auto maskc) __attribute__((always_inline)) {
+    // Row max of the raw scores (scale > 0 commutes with max); masked keys become -inf.
+    float mx = kNegInf;
+    if (full) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+    } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = st[kb][r] * scale_log2;
-          if constexpr (decltype(maskc)::value) {
-            if (!visible(my_q, j0 + 32 * kb + acc_row(r), S, causal, window)) x = kNegInf;
-          }
-          st[kb][r] = x;
-          tmax = fmaxf(tmax, x);
+          if (!visible(my_q, j0 + 32 * kb + acc_row(r), S, causal, window)) st[kb][r] = kNegInf;
+          mx = fmaxf(mx, st[kb][r]);
         }
       }
-    };
-    if (full) scale_mask(IC<0>{});
-    else scale_mask(IC<1>{});
-    tmax = pair_max(tmax);
-    const float m_new = fmaxf(m, tmax);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;  // row with nothing visible yet
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    }
+    mx = pair_max(mx) * scale_log2;
+    // Rescale a row only when its max grew by more than 2^8 (exponents stay <= 8, so P <= 256
+    // and every sum stays far from overflow; O / l does not depend on the reference value). The
+    // decision is per row, so a row's arithmetic never depends on other rows' keys; the multiply
+    // instructions are skipped when no row of the wave needs them (alpha = 1 is exact otherwise).
+    const bool grow = mx > m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? (m == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m - mx)) : 1.f;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    m = grow ? mx : m;
+    const float neg_m = m == kNegInf ? 0.f : -m;  // row with nothing visible yet: all P are 0
+
+    // P^T = exp2(S^T * scale*log2e - m) as element-type fragments; the row sum uses the same
+    // rounded values that enter O^T, so the normaliser matches the numerator.
+    Frag<E> pf[KB][2];
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(st[kb][r] - m_use);
-        st[kb][r] = p;
-        psum += p;
-      }
-    }
-    psum = pair_sum(psum);
-    l = l * alpha + psum;
-    m = m_new;
+      for (int r = 0; r < 16; ++r) st[kb][r] = __builtin_amdgcn_exp2f(fmaf(st[kb][r], scale_log2, neg_m));
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      for (int t = 0; t < 2; ++t) pf[kb][t] = acc_frag_sum<E>(st[kb], t, psum);
+    }
+    l += pair_sum(psum);
 
     // O^T += V^T P^T, contraction over the tile's keys in the accumulator's row order.
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const Frag<E> pf = acc_frag<E>(st[kb], t);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          mma(acc[db], TrFrag<E, KvTile>::get(v_lds, 32 * kb + 16 * t, 32 * db), pf);
-      }
-    }
+          mma(acc[db], TrFrag<E, KvTile>::get(v_lds, 32 * kb + 16 * t, 32 * db), pf[kb][t]);
   };
 
-  // One step: start the copy of tile s+1, wait for this wave's part of tile s, barrier, use s.
+  // One step: wait for this wave's part of tile s, barrier, start the copy of tile s+2 into the
+  // stage everyone finished with at step s-1, use tile s.
   auto step = [&](auto stc, int s) __attribute__((always_inline)) {
     constexpr int ST = decltype(stc)::value;
     char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
-    char* nxt = ST == 0 ? st1 : (ST == 1 ? st2 : st0);
-    if (s + 1 < n_steps) {
-      issue(s + 1, nxt);
-      wait_vmcnt<kOps>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    char* nn = ST == 0 ? st2 : (ST == 1 ? st0 : st1);
+    if (s + 1 < n_steps) wait_vmcnt<kOps>();
+    else wait_vmcnt<0>();
     barrier_keep_vm();
+    if (s + 2 < n_steps) issue(s + 2, nn);
     compute(s, cur);
   };
   for (int s = 0; s < n_steps; s += 3) {

@@ -100,6 +100,39 @@ template <> __device__ __forceinline__ Frag<F32> acc_frag<F32>(const f32x16_t& a
   return f;
 }
 
+// Accumulator registers 8t..8t+7 as an element-type fragment, adding the 8 rounded values to
+// `sum`. For bf16 the sum is four v_dot2c_f32_bf16 against (1, 1) on the packed words. The words
+// are kept as separate scalars before they form the vector: feeding elements extracted from the
+// assembled u32x4 to the dot2 builtin was miscompiled (the same word read four times).
+__device__ __forceinline__ Frag<BF16> acc_frag_sum(const f32x16_t& a, int t, float& sum) {
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+  const uint32_t w0 = pack_bf16x2(a[8 * t + 0], a[8 * t + 1]);
+  const uint32_t w1 = pack_bf16x2(a[8 * t + 2], a[8 * t + 3]);
+  const uint32_t w2 = pack_bf16x2(a[8 * t + 4], a[8 * t + 5]);
+  const uint32_t w3 = pack_bf16x2(a[8 * t + 6], a[8 * t + 7]);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(ones, __builtin_bit_cast(bf16x2_t, w0), sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(ones, __builtin_bit_cast(bf16x2_t, w1), sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(ones, __builtin_bit_cast(bf16x2_t, w2), sum, false);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(ones, __builtin_bit_cast(bf16x2_t, w3), sum, false);
+  Frag<BF16> f;
+  f.v = u32x4_t{w0, w1, w2, w3};
+  return f;
+}
+__device__ __forceinline__ Frag<F32> acc_frag_sum(const f32x16_t& a, int t, float& sum, F32*) {
+  Frag<F32> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.lo[e] = a[8 * t + e];
+    f.hi[e] = a[8 * t + 4 + e];
+    sum += f.lo[e] + f.hi[e];
+  }
+  return f;
+}
+template <class E> __device__ __forceinline__ Frag<E> acc_frag_sum(const f32x16_t& a, int t, float& sum) {
+  if constexpr (E::kBytes == 2) return acc_frag_sum(a, t, sum);
+  else return acc_frag_sum(a, t, sum, (F32*)nullptr);
+}
+
 // ---------------------------------------------------------------- global fragments
 // 8 consecutive elements from global memory (16 B for bf16, 32 B for f32), or zeros.
 __device__ __forceinline__ Frag<BF16> load_frag_global(const uint16_t* p, bool ok) {

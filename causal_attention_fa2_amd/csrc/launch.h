@@ -21,6 +21,7 @@ struct Args {
   void* dk;
   void* dv;
   float* delta;       // backward workspace: rowsum(dO * O), [B, Hq, S]
+  float* lse2;        // backward workspace: lse * log2(e), [B, Hq, S]
   float* part;        // backward workspace: fp32 dK / dV partial sums of the head-group parts
   int B, Hq, Hkv, S, D;
   int causal, window;
@@ -59,10 +60,11 @@ inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int S) {
 inline size_t delta_bytes(int B, int Hq, int S) {
   return ((size_t)B * Hq * S * sizeof(float) + 255) / 256 * 256;
 }
+// Workspace layout: delta [B,Hq,S] f32 | lse * log2(e) [B,Hq,S] f32 | dK/dV partials (if split).
 inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
   const DkdvPlan p = dkdv_plan(B, Hq, Hkv, S);
   size_t partials = p.hs > 1 ? (size_t)p.hs * 2 * B * Hkv * S * D * sizeof(float) : 0;
-  return delta_bytes(B, Hq, S) + partials;
+  return 2 * delta_bytes(B, Hq, S) + partials;
 }
 
 }  // namespace fa

@@ -63,8 +63,9 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
              void* stream);
 
 /* Bytes of device workspace attn_bwd needs for these sizes: the per-row delta = rowsum(dO * O)
- * (B*Hq*S fp32) and, when the dK/dV pass splits a query-head group across workgroups, fp32 partial
- * sums of dK and dV (2 * parts * B*Hkv*S*D fp32). Returns 0 for sizes attn_bwd would reject. */
+ * and lse * log2(e) (B*Hq*S fp32 each, 256-byte aligned) and, when the dK/dV pass splits a
+ * query-head group across workgroups, fp32 partial sums of dK and dV (2 * parts * B*Hkv*S*D
+ * fp32). Returns 0 for sizes attn_bwd would reject. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 
 /* Backward. o and lse must be exactly what attn_fwd wrote for the same q, k, v and arguments.

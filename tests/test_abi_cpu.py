@@ -63,12 +63,12 @@ def test_workspace_bytes(lib):
                 (1, 64, 8, 32768, 128), (1, 4, 2, 300, 64), (1, 2, 2, 64, 64)):
         B, Hq, Hkv, S, D = shp
         hs = _parts(B, Hq, Hkv, S)
-        delta = (B * Hq * S * 4 + 255) // 256 * 256
+        rows = (B * Hq * S * 4 + 255) // 256 * 256  # delta, then lse * log2(e)
         part = 2 * hs * B * Hkv * S * D * 4 if hs > 1 else 0
-        assert fa.attn_bwd_workspace_bytes(*shp) == delta + part, shp
+        assert fa.attn_bwd_workspace_bytes(*shp) == 2 * rows + part, shp
     assert _parts(1, 64, 8, 4096) == 2 and _parts(1, 64, 8, 32768) == 1
-    assert fa.attn_bwd_workspace_bytes(1, 64, 8, 4096, 128) == 64 * 4096 * 4 + 2 * 2 * 8 * 4096 * 128 * 4
-    assert fa.attn_bwd_workspace_bytes(1, 2, 2, 3, 64) == 256  # rounded up to 256 bytes
+    assert fa.attn_bwd_workspace_bytes(1, 64, 8, 4096, 128) == 2 * 64 * 4096 * 4 + 2 * 2 * 8 * 4096 * 128 * 4
+    assert fa.attn_bwd_workspace_bytes(1, 2, 2, 3, 64) == 512  # two row arrays, 256-byte aligned
     assert fa.attn_bwd_workspace_bytes(1, 3, 2, 64, 64) == 0   # Hq % Hkv != 0
     assert fa.attn_bwd_workspace_bytes(1, 2, 2, 64, 96) == 0   # unsupported D
 
