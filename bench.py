@@ -29,9 +29,9 @@ METRIC = "fwd+bwd causal attn TFLOP/s & % bf16 MFMA peak (GQA 64/8, d128, S=4096
 KERNEL_SOURCES = {
     "attn_fwd": ["attn_fwd.hip", "device.h", "tiles.h"],
     "attn_bwd_delta": ["attn_bwd.hip", "device.h"],
-    "attn_bwd_dkdv": ["attn_bwd.hip", "device.h", "tiles.h"],
+    "attn_bwd_dkdv": ["attn_dkdv.hip", "device.h", "tiles.h"],
     "attn_bwd_dq": ["attn_bwd.hip", "device.h", "tiles.h"],
-    "attn_bwd_dkdv_reduce": ["attn_bwd.hip", "device.h"],
+    "attn_bwd_dkdv_reduce": ["attn_dkdv.hip", "device.h"],
 }
 
 
@@ -93,7 +93,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa64x8-s4096-d128")
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="query heads in the CPU oracle sample (rounded to whole KV groups)")

@@ -1,0 +1,309 @@
+// attn_dkdv.hip -- dK / dV pass of the tiled causal / sliding-window GQA attention backward.
+//
+// Method: "KYNETRA FOUNDRY" page, FlashAttention paragraph (score tiles are recomputed in the
+// backward); "CUDA-LLM: A GitHub Repository for Development", section "The custom CUDA kernel"
+// (probabilities recomputed from the saved log-sum-exp); Grip paragraph of the first page (dK and
+// dV of a shared K/V head sum over its query-head group). The decomposition is described in
+// attn_bwd.hip. This translation unit is compiled with the MFMA results kept in VGPRs: the S / dP
+// products feed VALU work directly, and the dK / dV accumulators still fit beside them.
+#include "device.h"
+#include "launch.h"
+
+namespace fa {
+
+template <class E, int D, int NW, int QB>
+__global__ __launch_bounds__(NW * 64) void dkdv_kernel(
+    const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
+    const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
+    const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dK,
+    typename E::T* __restrict__ dV, float* __restrict__ part, int B, int Hq, int Hkv, int S,
+    int causal, int window, float scale, float scale_log2, int n_kt, int n_pairs, int hs) {
+  constexpr int BC = 32 * NW;  // keys per workgroup
+  constexpr int BR = 32 * QB;  // query rows per streamed tile
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  static_assert(NW >= 2, "two waves copy lse and delta");
+  typedef LdsTile<E, BR, D> QTile;
+  constexpr int kTileOps = dma_tile_ops<E, BR, D, NW>();
+  constexpr int kRowOff = 2 * QTile::kBytes;  // lse[64] then delta[64] (fp32)
+  constexpr int kStage = kRowOff + 512;
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kStage];
+
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  // Work item: (batch x KV head, head part, key-tile pair). Items are dealt to XCDs in contiguous
+  // chunks (dispatch is round-robin over the 8 XCDs) so the items of one KV head share an L2.
+  const int T = B * Hkv * hs * n_pairs;
+  const int wi = (T % 8 == 0) ? (int)(blockIdx.x % 8) * (T / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int pair = wi % n_pairs;
+  const int t2 = wi / n_pairs;
+  const int hp = t2 % hs;
+  const int bg = t2 / hs;
+  const int b = bg / Hkv;
+  const int G = Hq / Hkv;
+  const int hpg = G / hs;
+  const int h0 = (bg - b * Hkv) * G + hp * hpg;
+  const int ta = pair;
+  const int tb = n_kt - 1 - pair;
+  const bool two = tb > ta;
+  const size_t kv_off = (size_t)bg * S * D;
+
+  // Segment = one key tile: the workgroup runs key tile ta, then key tile tb.
+  int kt = ta, lo = 0, nq = 0, n_steps = 0;
+  auto set_segment = [&](int t) __attribute__((always_inline)) {
+    int hi;
+    kt = t;
+    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, BR, causal, window, &lo, &hi);
+    nq = hi - lo + 1;
+    n_steps = hpg * nq;
+  };
+  // step -> (query head, first query row) of the current segment
+  // Query tiles are visited from the last one down, so the workgroups of one KV head (which all
+  // end at the last query tile) sweep the same Q / dO tiles at about the same time. Steps run
+  // head by head; (hh, it) is a step's head offset and query-tile counter.
+  auto issue = [&](int hh, int it, char* stg) __attribute__((always_inline)) {
+    const int i0 = (lo + nq - 1 - it) * BR;
+    const size_t bh = (size_t)b * Hq + h0 + hh;
+    dma_tile<E, BR, D, NW>(stg, Q + bh * S * D, i0, S);
+    dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * S * D, i0, S);
+    if (w == 0) dma_row_floats(stg + kRowOff, LSE2 + bh * S, i0, S);
+    if (w == 1) dma_row_floats(stg + kRowOff + 256, delta + bh * S, i0, S);
+  };
+  auto advance = [&](int& hh, int& it) __attribute__((always_inline)) {
+    if (++it == nq) {
+      it = 0;
+      ++hh;
+    }
+  };
+
+  Frag<E> kf[DS], vf[DS];
+  f32x16_t dk[DB], dv[DB];
+  auto load_kv = [&]() __attribute__((always_inline)) {
+    const int my_k = kt * BC + 32 * w + l32;
+    const bool ok = my_k < S;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      kf[s] = load_frag_global(K + kv_off + (size_t)my_k * D + 16 * s + 8 * half, ok);
+      vf[s] = load_frag_global(V + kv_off + (size_t)my_k * D + 16 * s + 8 * half, ok);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dk[db] = f32x16_t{};
+      dv[db] = f32x16_t{};
+    }
+  };
+  // dk[db], dv[db]: register r holds key kw + acc_row(r), column 32*db + l32.
+  auto flush = [&]() __attribute__((always_inline)) {
+    const int kw = kt * BC + 32 * w;
+    const size_t nkv = (size_t)B * Hkv * S * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kw + acc_row(r);
+        if (key >= S) continue;
+        const size_t off = kv_off + (size_t)key * D + 32 * db + l32;
+        if (hs > 1) {
+          part[(size_t)(2 * hp) * nkv + off] = dk[db][r];
+          part[(size_t)(2 * hp + 1) * nkv + off] = dv[db][r];
+        } else if constexpr (E::kBytes == 2) {
+          dK[off] = (uint16_t)bf16_bits(dk[db][r] * scale);
+          dV[off] = (uint16_t)bf16_bits(dv[db][r]);
+        } else {
+          dK[off] = dk[db][r] * scale;
+          dV[off] = dv[db][r];
+        }
+      }
+    }
+  };
+
+  auto compute = [&](int it, const char* q_lds) __attribute__((always_inline)) {
+    const char* do_lds = q_lds + QTile::kBytes;
+    const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
+    const float* dl_lds = lse_lds + 64;
+    const int i0 = (lo + nq - 1 - it) * BR;
+    const int kw = kt * BC + 32 * w;
+    const int my_k = kw + l32;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int r0 = i0 + 32 * qb;
+      if (block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window)) continue;
+      const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window);
+      // All Q / dO row fragments of this block in flight before the S / dP products, so the
+      // LDS latency is paid once per block rather than once per MFMA.
+      Frag<E> qa[DS], da[DS];
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) {
+        qa[s2] = RowFrag<E, QTile>::get(q_lds, 32 * qb + l32, s2);
+        da[s2] = RowFrag<E, QTile>::get(do_lds, 32 * qb + l32, s2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16_t sa = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) {
+        mma(sa, qa[s2], kf[s2]);
+        mma(dp, da[s2], vf[s2]);
+      }
+      // The first half of the transposed dO / Q fragments travels during the softmax gradient.
+      Frag<E> tdo[DB], tq[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        tdo[db] = TrFrag<E, QTile>::get(do_lds, 32 * qb, 32 * db);
+        tq[db] = TrFrag<E, QTile>::get(q_lds, 32 * qb, 32 * db);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      auto softmax_grad = [&](auto maskc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rb = 32 * qb + 8 * r4 + 4 * half;  // registers 4*r4 .. 4*r4+3: rows rb .. rb+3
+          const f32x4_t lse4 = *reinterpret_cast<const f32x4_t*>(lse_lds + rb);
+          const f32x4_t dl4 = *reinterpret_cast<const f32x4_t*>(dl_lds + rb);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * r4 + c;
+            float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse4[c]));
+            if constexpr (decltype(maskc)::value) {
+              if (!visible(i0 + rb + c, my_k, S, causal, window)) p = 0.f;
+            }
+            sa[r] = p;
+            dp[r] = p * (dp[r] - dl4[c]);
+          }
+        }
+      };
+      if (full) softmax_grad(IC<0>{});
+      else softmax_grad(IC<1>{});
+      // dV += P^T dO, dK += dS^T Q (the second half's fragments are fetched under the first).
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const Frag<E> pf = acc_frag<E>(sa, t);
+        const Frag<E> sf = acc_frag<E>(dp, t);
+        Frag<E> ndo[DB], nq[DB];
+        if (t == 0) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            ndo[db] = TrFrag<E, QTile>::get(do_lds, 32 * qb + 16, 32 * db);
+            nq[db] = TrFrag<E, QTile>::get(q_lds, 32 * qb + 16, 32 * db);
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          mma(dv[db], pf, tdo[db]);
+          mma(dk[db], sf, tq[db]);
+        }
+        if (t == 0) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            tdo[db] = ndo[db];
+            tq[db] = nq[db];
+          }
+        }
+      }
+    }
+  };
+
+  // Step s: wait for this wave's part of tile s, barrier, start the copy of tile s+2 into the stage
+  // everyone finished with at step s-1, use tile s. (ch, ct) are step s's counters, (ih, iq) step
+  // s+2's.
+  int ch, ct, ih, iq;
+  auto step = [&](auto stc, int s) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stc)::value;
+    char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
+    char* nn = ST == 0 ? st2 : (ST == 1 ? st0 : st1);
+    if (s + 1 < n_steps) {
+      if (w < 2) wait_vmcnt<2 * kTileOps + 1>();
+      else wait_vmcnt<2 * kTileOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_keep_vm();
+    if (s + 2 < n_steps) {
+      issue(ih, iq, nn);
+      advance(ih, iq);
+    }
+    compute(ct, cur);
+    advance(ch, ct);
+  };
+  const int n_seg = two ? 2 : 1;
+  for (int seg = 0; seg < n_seg; ++seg) {
+    if (seg) barrier_keep_vm();  // every wave is done with the previous segment's stages
+    set_segment(seg ? tb : ta);
+    load_kv();
+    ch = 0, ct = 0, ih = 0, iq = 0;
+    issue(ih, iq, st0);
+    advance(ih, iq);
+    if (n_steps > 1) {
+      issue(ih, iq, st1);
+      advance(ih, iq);
+    }
+    wait_vmcnt<0>();
+    for (int s = 0; s < n_steps; s += 3) {
+      step(IC<0>{}, s);
+      if (s + 1 < n_steps) step(IC<1>{}, s + 1);
+      if (s + 2 < n_steps) step(IC<2>{}, s + 2);
+    }
+    flush();
+  }
+}
+
+template <class E>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
+                                                          typename E::T* __restrict__ dK,
+                                                          typename E::T* __restrict__ dV,
+                                                          size_t n, int hs, float scale) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4_t sk = *reinterpret_cast<const f32x4_t*>(part + i);
+  f32x4_t sv = *reinterpret_cast<const f32x4_t*>(part + n + i);
+  for (int p = 1; p < hs; ++p) {
+    sk += *reinterpret_cast<const f32x4_t*>(part + (size_t)(2 * p) * n + i);
+    sv += *reinterpret_cast<const f32x4_t*>(part + (size_t)(2 * p + 1) * n + i);
+  }
+  sk *= scale;
+  if constexpr (E::kBytes == 2) {
+    *reinterpret_cast<u32x2_t*>(dK + i) = u32x2_t{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
+    *reinterpret_cast<u32x2_t*>(dV + i) = u32x2_t{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+  } else {
+    *reinterpret_cast<f32x4_t*>(dK + i) = sk;
+    *reinterpret_cast<f32x4_t*>(dV + i) = sv;
+  }
+}
+
+template <class E, int D>
+static int launch_dkdv_t(const Args& a) {
+  {
+    hipStream_t st = (hipStream_t)a.stream;
+    typedef typename E::T T;
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    constexpr int NW = kDkdvWaves;
+    constexpr int QB = E::kBytes == 2 ? 2 : 1;
+    const DkdvPlan p = dkdv_plan(a.B, a.Hq, a.Hkv, a.S);
+    dim3 grid((unsigned)(p.n_pairs * a.B * a.Hkv * p.hs)), block(NW * 64);
+    notify_launch("attn_bwd_dkdv", 0, a.stream);
+    hipLaunchKernelGGL((dkdv_kernel<E, D, NW, QB>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
+                       (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.S, a.causal, a.window, a.scale,
+                       scale_log2, p.n_kt, p.n_pairs, p.hs);
+    notify_launch("attn_bwd_dkdv", 1, a.stream);
+    if (p.hs > 1) {
+      const size_t n = (size_t)a.B * a.Hkv * a.S * D;
+      dim3 rgrid((unsigned)((n / 4 + 255) / 256)), rblock(256);
+      notify_launch("attn_bwd_dkdv_reduce", 0, a.stream);
+      hipLaunchKernelGGL((dkdv_reduce_kernel<E>), rgrid, rblock, 0, st, (const float*)a.part,
+                         (T*)a.dk, (T*)a.dv, n, p.hs, a.scale);
+      notify_launch("attn_bwd_dkdv_reduce", 1, a.stream);
+    }
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_dkdv(const Args& a) {
+  if (a.dtype == kBF16) return a.D == 64 ? launch_dkdv_t<BF16, 64>(a) : launch_dkdv_t<BF16, 128>(a);
+  return a.D == 64 ? launch_dkdv_t<F32, 64>(a) : launch_dkdv_t<F32, 128>(a);
+}
+
+}  // namespace fa

@@ -333,15 +333,28 @@ __device__ __forceinline__ void dma_tile(char* lds, const typename E::T* __restr
   const int lane = lane_id();
   const int w = wave_id();
   const uint32_t base = lds_addr(lds);
+  const char* tile = reinterpret_cast<const char*>(src + (size_t)row0 * D);
+  if (row0 + ROWS <= S) {
+    // Whole tile in range: per-lane byte offsets inside the tile do not depend on row0.
 #pragma unroll
-  for (int n = 0; n < kBlocks / NW; ++n) {
-    const int blk = n * NW + w;
-    const int c = blk * 64 + lane;
-    const int r = c / Tile::kChunks;
-    const int pos = c % Tile::kChunks;
-    const int gr = imin_(row0 + r, S - 1);
-    const char* g = reinterpret_cast<const char*>(src + (size_t)gr * D) + ((pos ^ Tile::swz(r)) << 4);
-    dma16(g, base + blk * 1024);
+    for (int n = 0; n < kBlocks / NW; ++n) {
+      const int blk = n * NW + w;
+      const int c = blk * 64 + lane;
+      const int r = c / Tile::kChunks;
+      const int pos = c % Tile::kChunks;
+      dma16(tile + r * Tile::kRowBytes + ((pos ^ Tile::swz(r)) << 4), base + blk * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < kBlocks / NW; ++n) {
+      const int blk = n * NW + w;
+      const int c = blk * 64 + lane;
+      const int r = c / Tile::kChunks;
+      const int pos = c % Tile::kChunks;
+      const int gr = imin_(row0 + r, S - 1);
+      const char* g = reinterpret_cast<const char*>(src + (size_t)gr * D) + ((pos ^ Tile::swz(r)) << 4);
+      dma16(g, base + blk * 1024);
+    }
   }
 }
 template <class E, int ROWS, int D, int NW>

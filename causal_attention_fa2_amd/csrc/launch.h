@@ -36,6 +36,7 @@ void notify_launch(const char* kernel, int after, void* stream);
 // Each returns 0 on success, -1 if the HIP runtime reported a launch error.
 int launch_fwd(const Args& a);
 int launch_bwd(const Args& a);
+int launch_dkdv(const Args& a);  // dK / dV pass (and its reduce), called by launch_bwd
 
 // dK/dV decomposition: a workgroup of kDkdvWaves waves owns 32*kDkdvWaves keys and processes key
 // tile j and then key tile n_kt-1-j (equal work per workgroup under the causal mask). When that
