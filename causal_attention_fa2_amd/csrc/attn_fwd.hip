@@ -10,9 +10,9 @@
 //   * each wave owns 32 query rows; its Q rows stay in registers for the whole kernel as the
 //     B operand of S^T = K Q^T (one accumulator column per query, so every lane owns one query:
 //     the row max / row sum are in-lane plus one permlane32 swap with the partner lane);
-//   * key / value tiles of 32*KB rows stream through a 3-stage ring of swizzled LDS tiles filled
-//     by LDS-DMA (global_load_lds_dwordx4): the copies of tiles s+1 and s+2 are in flight while
-//     tile s is used, with one workgroup barrier per tile;
+//   * key / value tiles of 32*KB rows stream through a ring of NST swizzled LDS tiles filled by
+//     LDS-DMA (global_load_lds_dwordx4): the next NST-1 tiles are in flight while tile s is used,
+//     with one workgroup barrier per tile;
 //   * P^T stays in registers and is the B operand of O^T = V^T P^T; V^T comes from LDS with the
 //     gfx950 transposing read, so V is never transposed in memory;
 //   * key tiles outside a wave's causal / window band are skipped, only boundary tiles are masked;
@@ -26,8 +26,8 @@
 
 namespace fa {
 
-template <class E, int D, int NW, int KB>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(
+template <class E, int D, int NW, int KB, int NST>
+__global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
     int B, int Hq, int Hkv, int S, int causal, int window, float scale_log2, int n_qt) {
@@ -38,9 +38,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   typedef LdsTile<E, BC, D> KvTile;
   constexpr int kStage = 2 * KvTile::kBytes;
   constexpr int kOps = 2 * dma_tile_ops<E, BC, D, NW>();  // DMA instructions per wave per stage
-  __shared__ __attribute__((aligned(1024))) char st0[kStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kStage];
-  __shared__ __attribute__((aligned(1024))) char st2[kStage];
+  static_assert(NST == 2 || NST == 3, "ring depth");
+  __shared__ __attribute__((aligned(1024))) char ring[NST * kStage];
 
   const int lane = lane_id();
   const int w = wave_id();
@@ -76,8 +75,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
     dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
   };
-  issue(0, st0);
-  if (n_steps > 1) issue(1, st1);
+  issue(0, ring);
+  if (NST == 3 && n_steps > 1) issue(1, ring + kStage);
 
   Frag<E> qf[DS];
 #pragma unroll
@@ -90,20 +89,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   float m = kNegInf;  // running max of base-2 scores
   float l = 0.f;      // running sum of exp2(score - m)
 
-  auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
+  auto compute_general = [&](int j0, const char* k_lds, bool full) __attribute__((always_inline)) {
     const char* v_lds = k_lds + KvTile::kBytes;
-    const int j0 = (jt_lo + s) * BC;
-    if (block_empty(qw, qw + 31, j0, j0 + BC - 1, S, causal, window)) return;
-    const bool full = block_full(qw, qw + 31, j0, j0 + BC - 1, S, causal, window);
 
-    // S^T = K Q^T for KB blocks of 32 keys: lane owns query my_q, registers hold keys.
+    // S^T = K Q^T for KB blocks of 32 keys: lane owns query my_q, registers hold keys. Each key
+    // block's K fragments are all requested before its products (LDS latency paid once).
     f32x16_t st[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      Frag<E> kfr[DS];
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) kfr[s2] = RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s2);
+      __builtin_amdgcn_sched_barrier(0);
       st[kb] = f32x16_t{};
 #pragma unroll
-      for (int s2 = 0; s2 < DS; ++s2) mma(st[kb], RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s2), qf[s2]);
+      for (int s2 = 0; s2 < DS; ++s2) mma(st[kb], kfr[s2], qf[s2]);
     }
+    // The first key block's V^T fragments travel during the softmax.
+    Frag<E> vt[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vt[db] = TrFrag<E, KvTile>::get(v_lds, 0, 32 * db);
+    __builtin_amdgcn_sched_barrier(0);
 
     // Row max of the raw scores (scale > 0 commutes with max); masked keys become -inf.
     float mx = kNegInf;
@@ -150,33 +156,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     }
     l += pair_sum(psum);
 
-    // O^T += V^T P^T, contraction over the tile's keys in the accumulator's row order.
+    // O^T += V^T P^T, contraction over the tile's keys in the accumulator's row order; the next
+    // 16 keys' V^T fragments are requested under the current products.
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int kt2 = 0; kt2 < 2 * KB; ++kt2) {
+      Frag<E> nv[DB];
+      if (kt2 + 1 < 2 * KB) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int db = 0; db < DB; ++db) nv[db] = TrFrag<E, KvTile>::get(v_lds, 16 * (kt2 + 1), 32 * db);
+      }
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          mma(acc[db], TrFrag<E, KvTile>::get(v_lds, 32 * kb + 16 * t, 32 * db), pf[kb][t]);
+      for (int db = 0; db < DB; ++db) mma(acc[db], vt[db], pf[kt2 / 2][kt2 % 2]);
+      if (kt2 + 1 < 2 * KB) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vt[db] = nv[db];
+      }
+    }
   };
 
-  // One step: wait for this wave's part of tile s, barrier, start the copy of tile s+2 into the
-  // stage everyone finished with at step s-1, use tile s.
-  auto step = [&](auto stc, int s) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stc)::value;
-    char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
-    char* nn = ST == 0 ? st2 : (ST == 1 ? st0 : st1);
-    if (s + 1 < n_steps) wait_vmcnt<kOps>();
-    else wait_vmcnt<0>();
-    barrier_keep_vm();
-    if (s + 2 < n_steps) issue(s + 2, nn);
-    compute(s, cur);
+  auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
+    const int j0 = (jt_lo + s) * BC;
+    if (block_empty(qw, qw + 31, j0, j0 + BC - 1, S, causal, window)) return;
+    compute_general(j0, k_lds, block_full(qw, qw + 31, j0, j0 + BC - 1, S, causal, window));
   };
-  for (int s = 0; s < n_steps; s += 3) {
-    step(IC<0>{}, s);
-    if (s + 1 < n_steps) step(IC<1>{}, s + 1);
-    if (s + 2 < n_steps) step(IC<2>{}, s + 2);
-  }
+
+  ring_run<NST, kStage, kOps>(ring, n_steps, issue, compute);
 
   if (!q_ok) return;
   const float inv_l = 1.f / l;
@@ -200,12 +204,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 
 template <class E, int D>
 static int launch_fwd_t(const Args& a) {
-  constexpr int NW = E::kBytes == 2 ? 8 : 4;
+  constexpr int NW = E::kBytes == 2 ? kFwdWaves : 4;
   constexpr int KB = E::kBytes == 2 ? 2 : 1;
+  constexpr int NST = E::kBytes == 2 ? kFwdStages : 3;
   const int n_qt = (a.S + 32 * NW - 1) / (32 * NW);
   dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
   notify_launch("attn_fwd", 0, a.stream);
-  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB>), grid, block, 0, (hipStream_t)a.stream,
+  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NST>), grid, block, 0, (hipStream_t)a.stream,
                      (const typename E::T*)a.q, (const typename E::T*)a.k, (const typename E::T*)a.v,
                      (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.causal, a.window,
                      (float)((double)a.scale * 1.4426950408889634), n_qt);

@@ -366,6 +366,35 @@ __device__ __forceinline__ void dma_row_floats(char* lds, const float* __restric
   dma4(src + r, lds_addr(lds));
 }
 
+// Runs steps 0 .. n-1 over an NST-stage ring of SB-byte LDS stages whose first NST-1 tiles were
+// already issued (and waited for) by the caller. Step s: wait until this wave's copies of tile s
+// have landed (OPS copy instructions per wave per tile; tiles s+1 .. s+NST-2 may stay in flight),
+// workgroup barrier, issue tile s+NST-1 into the stage every wave finished with at step s-1, then
+// compute on tile s. One barrier per step; tile s+NST-1 is fetched while tiles s.. are used.
+template <int NST, int SB, int OPS, class Issue, class Compute>
+__device__ __forceinline__ void ring_run(char* ring, int n, Issue&& issue, Compute&& compute) {
+  static_assert(NST == 2 || NST == 3, "ring depth");
+  auto one = [&](auto kc, int s) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (NST == 3) {
+      if (s + 1 < n) wait_vmcnt<OPS>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_keep_vm();
+    if (s + NST - 1 < n) issue(s + NST - 1, ring + ((k + NST - 1) % NST) * SB);
+    compute(s, ring + k * SB);
+  };
+  for (int s0 = 0; s0 < n; s0 += NST) {
+    one(IC<0>{}, s0);
+    if (s0 + 1 < n) one(IC<1>{}, s0 + 1);
+    if constexpr (NST == 3) {
+      if (s0 + 2 < n) one(IC<2>{}, s0 + 2);
+    }
+  }
+}
+
 // Accumulator row index (within a 32 x 32 tile) held in register r by this lane.
 __device__ __forceinline__ int acc_row(int r) { return 8 * (r >> 2) + 4 * (lane_id() >> 5) + (r & 3); }
 

@@ -38,6 +38,16 @@ int launch_fwd(const Args& a);
 int launch_bwd(const Args& a);
 int launch_dkdv(const Args& a);  // dK / dV pass (and its reduce), called by launch_bwd
 
+// Forward workgroup shape for bf16: waves per workgroup (32 query rows each) and LDS ring depth
+// (tiles in flight + 1).
+#ifndef ATTN_FWD_WAVES
+#define ATTN_FWD_WAVES 8
+#endif
+#ifndef ATTN_FWD_STAGES
+#define ATTN_FWD_STAGES 3
+#endif
+constexpr int kFwdWaves = ATTN_FWD_WAVES, kFwdStages = ATTN_FWD_STAGES;
+
 // dK/dV decomposition: a workgroup of kDkdvWaves waves owns 32*kDkdvWaves keys and processes key
 // tile j and then key tile n_kt-1-j (equal work per workgroup under the causal mask). When that
 // gives fewer than kDkdvMinGroups workgroups, the query-head group is split into `hs` parts (a
