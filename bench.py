@@ -67,6 +67,46 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def device_peak_bf16(torch):
+    """CUs x 4096 bf16 FLOP/clk/CU x the clock the HIP runtime reports, in TFLOP/s (or None)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded (same soname)
+        val = ctypes.c_int(0)
+        dev = torch.cuda.current_device()
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, dev) != 0:  # hipDeviceAttributeClockRate
+            return None
+        clock_khz = val.value
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 63, dev) != 0:  # ...MultiprocessorCount
+            return None
+        return {"cus": val.value, "clock_mhz": clock_khz / 1e3,
+                "tflops": round(val.value * 4096 * clock_khz * 1e3 / 1e12, 1)}
+    except OSError:
+        return None
+
+
+def host_info():
+    """CPU model and the BLAS numpy uses, for the oracle timing."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                if p.get("user_api") == "blas"]
+        blas = ", ".join(libs) or None
+    except Exception:
+        pass
+    return model, blas
+
+
 def cpu_baseline(w, q, k, v, do, heads: int):
     """The fp64 oracle, timed on this host's cores, on the first `heads` query heads (whole KV
     groups) of the same inputs."""
@@ -84,9 +124,11 @@ def cpu_baseline(w, q, k, v, do, heads: int):
                             w.causal, w.window, w.scale)
     dt = time.perf_counter() - t0
     flops = 4.0 * w.B * heads * attended_pairs(w.S, w.causal, w.window) * w.D * 3.5
+    model, blas = host_info()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle fwd+bwd on {heads} of {w.Hq} query heads ({groups} KV groups), "
-                      f"B={w.B}, S={w.S}, D={w.D}: {dt:.2f} s wall"}
+                      f"B={w.B}, S={w.S}, D={w.D}: {dt:.2f} s wall",
+            "cpu_model": model, "blas": blas}
 
 
 def main() -> int:
@@ -150,12 +192,34 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
+    # fwd, bwd and fwd+bwd separately: HIP events on the launch stream around each repetition
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            out.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in out)
+        return {"median": round(ms[len(ms) // 2], 4), "min": round(ms[0], 4)}
+
+    phases = {
+        "fwd": timed(lambda: fa.attn_fwd(tq, tk, tv, o, lse, w.causal, w.window, w.scale), args.steps),
+        "bwd": timed(lambda: fa.attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window,
+                                         w.scale), args.steps),
+        "fwd+bwd": timed(step, args.steps),
+    }
+
     # per-kernel durations: HIP events recorded on the launch stream around each kernel
     events = {}
 
-    def hook(kernel, after, stream):
+    def hook(kernel, after, hip_stream):
         ev = torch.cuda.Event(enable_timing=True)
-        ev.record(torch.cuda.current_stream())
+        ev.record(stream)  # the library launches on torch's current stream (passed as hip_stream)
         events.setdefault(kernel, []).append(ev)
 
     fa.attn_set_launch_hook(hook)
@@ -175,6 +239,7 @@ def main() -> int:
     unit = 2.0 * w.B * w.Hq * N * w.D  # one GEMM-sized pass over the attended pairs
     fl = {"attn_fwd": 2 * unit, "attn_bwd_dkdv": 4 * unit, "attn_bwd_dq": 1 * unit}
     total_flops = 7 * unit  # forward (2) + backward counted as 2.5x forward (5)
+    fl_fwd, fl_bwd = 2 * unit, 5 * unit
     value = total_flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     eb = 2 if w.dtype == "bf16" else 4
@@ -212,6 +277,12 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
                    "causal": w.causal, "window": w.window, "parallelism": "none (1 GPU)"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "phase_ms": phases,
+        "phase_tflops_median": {
+            "fwd": round(fl_fwd / (phases["fwd"]["median"] * 1e-3) / 1e12, 1),
+            "bwd": round(fl_bwd / (phases["bwd"]["median"] * 1e-3) / 1e12, 1),
+            "fwd+bwd": round(total_flops / (phases["fwd+bwd"]["median"] * 1e-3) / 1e12, 1)},
+        "device_peak_bf16": device_peak_bf16(torch),
         "ms_per_step_with_kernel_events": round(ms_hooked, 4),
         "kernels": kernels,
         "roofline": roof,
