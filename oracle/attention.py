@@ -19,6 +19,9 @@ What it computes is plain materialised softmax attention and its exact gradient,
     backward recomputes the softmax probabilities from the saved log-sum-exp.
   * "From-scratch GPU LLM training", section "What is built": scaled-dot-product attention is one of
     the gradient kernels, checked tensor by tensor against a CPU reference.
+  * "CUDA-LLM: A GitHub Repository for Development", section "The custom CUDA kernel": the kernel is
+    generalised to fewer queries than keys (S_q <= S_k), so that one kernel serves a full prefill and
+    a single-token decode against a cache.
 
 Readings where the pages leave a step open (each also listed in the design notes):
   * tensors are [B, H, S, D] contiguous, D fastest; K and V have Hkv heads, Q/O/dO have Hq heads;
@@ -28,7 +31,10 @@ Readings where the pages leave a step open (each also listed in the design notes
     rejected;
   * `scale` multiplies Q K^T before the softmax; the saved log-sum-exp is the natural log of the sum
     of exponentials of the *scaled* scores;
-  * every row has at least one visible key (the diagonal), so no empty-row convention is needed.
+  * with S_q <= S_k the queries are the last S_q positions: query i sits at absolute position
+    i + (S_k - S_q) for the causal mask and the window ("bottom-right" alignment; a single decode query
+    sees every key); S_q > S_k is not defined by the pages and is rejected;
+  * every row has at least one visible key (its own position), so no empty-row convention is needed.
 
 Rows are processed in blocks of `row_block` queries only to bound memory: each row's softmax is
 normalised over that row alone, so a row's outputs depend only on that row; dK and dV sum the
@@ -47,11 +53,15 @@ __all__ = [
 
 
 def _check(q, k, v, causal, window):
+    """Returns (B, Hq, Hkv, S_q, S_k, D)."""
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be [B, H, S, D]")
-    B, Hq, S, D = q.shape
-    if k.shape[0] != B or k.shape[2:] != (S, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [B, Hkv, S, D] with q's B, S, D")
+    B, Hq, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, S_k, D] with q's B and D")
+    if Sq > Sk:
+        raise ValueError("fewer keys than queries (S_q > S_k) is not defined")
     Hkv = k.shape[1]
     if Hkv < 1 or Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
@@ -59,7 +69,7 @@ def _check(q, k, v, causal, window):
         raise ValueError("window must be >= 0")
     if window > 0 and not causal:
         raise ValueError("a sliding window requires the causal mask")
-    return B, Hq, Hkv, S, D
+    return B, Hq, Hkv, Sq, Sk, D
 
 
 def kv_head(h: int, Hq: int, Hkv: int) -> int:
@@ -67,10 +77,10 @@ def kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def visible_mask(rows, cols, causal: bool, window: int) -> np.ndarray:
-    """Boolean [len(rows), len(cols)]: key j is visible to query i iff (not causal or j <= i)
-    and (window == 0 or i - j < window)."""
-    i = np.asarray(rows, dtype=np.int64)[:, None]
+def visible_mask(rows, cols, causal: bool, window: int, offset: int = 0) -> np.ndarray:
+    """Boolean [len(rows), len(cols)]: with query i at position p = i + offset, key j is visible
+    iff (not causal or j <= p) and (window == 0 or p - j < window). offset = S_k - S_q."""
+    i = np.asarray(rows, dtype=np.int64)[:, None] + offset
     j = np.asarray(cols, dtype=np.int64)[None, :]
     m = np.ones((i.shape[0], j.shape[1]), dtype=bool)
     if causal:
@@ -80,23 +90,23 @@ def visible_mask(rows, cols, causal: bool, window: int) -> np.ndarray:
     return m
 
 
-def visible_count(i: int, S: int, causal: bool, window: int) -> int:
-    """Number of keys visible to query i (counted from the mask definition)."""
-    return int(visible_mask([i], np.arange(S), causal, window).sum())
+def visible_count(i: int, S: int, causal: bool, window: int, offset: int = 0) -> int:
+    """Number of the S keys visible to query i (counted from the mask definition)."""
+    return int(visible_mask([i], np.arange(S), causal, window, offset).sum())
 
 
-def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None):
-    """One head, a set of query rows, all S keys.
+def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0):
+    """One head, a set of query rows, all S_k keys.
 
-    qh [S, D], kh/vh [S, D], doh [S, D] or None (float64). Returns a dict with
-    P [R, S] (softmax probabilities, exactly 0 where masked), O [R, D], LSE [R],
-    and when doh is given dP [R, S], delta [R] and dS [R, S]."""
+    qh [S_q, D], kh/vh [S_k, D], doh [S_q, D] or None (float64); query i at position i + offset.
+    Returns a dict with P [R, S_k] (softmax probabilities, exactly 0 where masked), O [R, D],
+    LSE [R], and when doh is given dP [R, S_k], delta [R] and dS [R, S_k]."""
     S = kh.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
-    mask = visible_mask(rows, np.arange(S), causal, window)
+    mask = visible_mask(rows, np.arange(S), causal, window, offset)
     x = scale * (qh[rows] @ kh.T)                     # scaled scores
     x = np.where(mask, x, -np.inf)
-    m = x.max(axis=1, keepdims=True)                  # finite: the diagonal is visible
+    m = x.max(axis=1, keepdims=True)                  # finite: the row's own position is visible
     e = np.exp(x - m)                                 # exp(-inf) == 0 exactly for masked keys
     l = e.sum(axis=1, keepdims=True)
     p = e / l
@@ -117,8 +127,9 @@ def _f64(*xs):
 def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256):
     """Full attention forward (O, LSE) and, when do is given, backward (dQ, dK, dV).
 
-    q, do [B,Hq,S,D]; k, v [B,Hkv,S,D]. Returns float64 arrays in a dict."""
-    B, Hq, Hkv, S, D = _check(q, k, v, causal, window)
+    q, do [B,Hq,S_q,D]; k, v [B,Hkv,S_k,D] with S_q <= S_k. Returns float64 arrays in a dict."""
+    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window)
+    off = Sk - S
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     q, k, v = _f64(q, k, v)
     O = np.zeros((B, Hq, S, D))
@@ -136,7 +147,7 @@ def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_bl
             for r0 in range(0, S, row_block):
                 rows = np.arange(r0, min(S, r0 + row_block))
                 t = head_rows(q[b, h], k[b, g], v[b, g], rows, causal, window, scale,
-                              None if do is None else do[b, h])
+                              None if do is None else do[b, h], off)
                 O[b, h, rows] = t["O"]
                 LSE[b, h, rows] = t["LSE"]
                 if do is not None:
@@ -160,43 +171,43 @@ def backward(q, k, v, do, causal=True, window=0, scale=None, row_block=256):
 
 
 def probabilities(q, k, b, h, causal=True, window=0, scale=None):
-    """Softmax probabilities P [S, S] of one (batch, query head)."""
+    """Softmax probabilities P [S_q, S_k] of one (batch, query head)."""
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     qh, kh = _f64(q[b, h], k[b, kv_head(h, Hq, Hkv)])
-    return head_rows(qh, kh, kh, np.arange(S), causal, window, scale)["P"]
+    return head_rows(qh, kh, kh, np.arange(S), causal, window, scale, None, k.shape[2] - S)["P"]
 
 
 def rows_forward(q, k, v, b, h, rows, causal=True, window=0, scale=None):
     """O[b, h, rows] and LSE[b, h, rows], each row computed on its own."""
-    B, Hq, Hkv, S, D = _check(q, k, v, causal, window)
+    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     g = kv_head(h, Hq, Hkv)
     qh, kh, vh = _f64(q[b, h], k[b, g], v[b, g])
-    t = head_rows(qh, kh, vh, rows, causal, window, scale)
+    t = head_rows(qh, kh, vh, rows, causal, window, scale, None, Sk - S)
     return t["O"], t["LSE"]
 
 
 def rows_dq(q, k, v, do, b, h, rows, causal=True, window=0, scale=None):
     """dQ[b, h, rows]: each row needs only its own probabilities and dP row."""
-    B, Hq, Hkv, S, D = _check(q, k, v, causal, window)
+    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     g = kv_head(h, Hq, Hkv)
     qh, kh, vh, doh = _f64(q[b, h], k[b, g], v[b, g], do[b, h])
-    t = head_rows(qh, kh, vh, rows, causal, window, scale, doh)
+    t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S)
     return scale * (t["dS"] @ kh)
 
 
 def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_block=256):
     """dK[b, g, cols] and dV[b, g, cols]: sums over every query head of group g and every
     query row that can see at least one of `cols`."""
-    B, Hq, Hkv, S, D = _check(q, k, v, causal, window)
+    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     cols = np.asarray(cols, dtype=np.int64)
     G = Hq // Hkv
     kh, vh = _f64(k[b, g], v[b, g])
-    need = visible_mask(np.arange(S), cols, causal, window).any(axis=1)
+    need = visible_mask(np.arange(S), cols, causal, window, Sk - S).any(axis=1)
     rows_all = np.nonzero(need)[0]
     dK = np.zeros((cols.size, D))
     dV = np.zeros((cols.size, D))
@@ -204,7 +215,7 @@ def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_bl
         qh, doh = _f64(q[b, h], do[b, h])
         for r0 in range(0, rows_all.size, row_block):
             rows = rows_all[r0:r0 + row_block]
-            t = head_rows(qh, kh, vh, rows, causal, window, scale, doh)
+            t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S)
             dK += scale * (t["dS"][:, cols].T @ qh[rows])
             dV += t["P"][:, cols].T @ doh[rows]
     return dK, dV

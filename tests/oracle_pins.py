@@ -10,7 +10,10 @@ a transposed operand, an off-by-one mask -- fails at least one of them):
   * torch's own float64 scaled_dot_product_attention and autograd on the CPU (a library routine);
   * closed forms: constant V, identical keys, window 1, zero queries, a hand-derived three-token case;
   * invariants: probability rows sum to 1, sum_j dS_ij = 0, sum_j dV_j = sum_i dO_i, keys outside
-    a row's visible set cannot change that row.
+    a row's visible set cannot change that row;
+  * fewer queries than keys (S_q < S_k): a chunk of queries equals the last S_q rows of the square
+    problem over all S_k positions (gradients with dO zero on the other rows), torch's own
+    lower-right causal bias, and a single decode query that sees every key (or the last W).
 """
 from __future__ import annotations
 
@@ -22,11 +25,13 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def _rng_inputs(seed, B, Hq, Hkv, S, D, std=1.0):
+def _rng_inputs(seed, B, Hq, Hkv, S, D, std=1.0, Sk=None):
+    """Q / dO have S rows, K / V have Sk (default S)."""
+    Sk = S if Sk is None else Sk
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, S, D)) * std
-    k = rng.standard_normal((B, Hkv, S, D)) * std
-    v = rng.standard_normal((B, Hkv, S, D))
+    k = rng.standard_normal((B, Hkv, Sk, D)) * std
+    v = rng.standard_normal((B, Hkv, Sk, D))
     do = rng.standard_normal((B, Hq, S, D))
     return q, k, v, do
 
@@ -98,9 +103,10 @@ def pin_fd_sampled(A, seed=1, n_entries=256, n_dirs=16, tol=1e-6):
 
 # ---------------------------------------------------------------- scalar brute force
 def _brute(q, k, v, do, causal, window, scale):
-    """Pure-Python loops; softmax derivative through the full Jacobian dP_k/dx_j = P_k (d_kj - P_j)."""
+    """Pure-Python loops; softmax derivative through the full Jacobian dP_k/dx_j = P_k (d_kj - P_j).
+    With Sq queries and Sk keys, query i stands at position i + Sk - Sq."""
     B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+    Hkv, Sk = k.shape[1], k.shape[2]
     G = Hq // Hkv
     O = np.zeros(q.shape)
     L = np.zeros((B, Hq, S))
@@ -111,8 +117,9 @@ def _brute(q, k, v, do, causal, window, scale):
         for h in range(Hq):
             g = h // G
             for i in range(S):
-                vis = [j for j in range(S)
-                       if (not causal or j <= i) and (window == 0 or i - j < window)]
+                pos = i + Sk - S
+                vis = [j for j in range(Sk)
+                       if (not causal or j <= pos) and (window == 0 or pos - j < window)]
                 x = {j: scale * sum(q[b, h, i, d] * k[b, g, j, d] for d in range(D)) for j in vis}
                 mx = max(x.values())
                 z = sum(math.exp(x[j] - mx) for j in vis)
@@ -132,18 +139,21 @@ def _brute(q, k, v, do, causal, window, scale):
 
 
 def pin_bruteforce(A, tol=1e-12):
-    for (B, Hq, Hkv, S, D, causal, window, seed) in (
-        (1, 2, 2, 7, 3, True, 0, 3), (2, 4, 2, 9, 4, True, 3, 4), (1, 3, 1, 6, 2, False, 0, 5),
-        (1, 4, 4, 8, 5, True, 1, 6), (1, 2, 1, 5, 3, True, 9, 7),
+    for (B, Hq, Hkv, S, Sk, D, causal, window, seed) in (
+        (1, 2, 2, 7, 7, 3, True, 0, 3), (2, 4, 2, 9, 9, 4, True, 3, 4), (1, 3, 1, 6, 6, 2, False, 0, 5),
+        (1, 4, 4, 8, 8, 5, True, 1, 6), (1, 2, 1, 5, 5, 3, True, 9, 7),
+        (1, 2, 1, 3, 8, 3, True, 0, 8), (2, 4, 2, 4, 9, 2, True, 3, 9), (1, 2, 2, 1, 6, 3, True, 0, 10),
+        (1, 2, 1, 1, 7, 2, True, 2, 14), (1, 3, 3, 4, 6, 2, False, 0, 15),
     ):
-        q, k, v, do = _rng_inputs(seed, B, Hq, Hkv, S, D)
+        q, k, v, do = _rng_inputs(seed, B, Hq, Hkv, S, D, Sk=Sk)
         scale = 0.7
         r = A.forward_backward(q, k, v, do, causal, window, scale)
         ref = _brute(q, k, v, do, causal, window, scale)
         for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"),
                               (r["O"], r["LSE"], r["dQ"], r["dK"], r["dV"]), ref):
             err = np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30)
-            assert err <= tol, f"brute force {name} (S={S}, W={window}, causal={causal}): {err:.3e}"
+            assert err <= tol, (f"brute force {name} (S={S}, Sk={Sk}, W={window}, causal={causal}): "
+                                f"{err:.3e}")
 
 
 # ---------------------------------------------------------------- library routine
@@ -245,20 +255,27 @@ def pin_window_one(A):
 
 def pin_zero_queries(A):
     """Q = 0: every visible score is 0, so exp(LSE_i) is exactly the number of visible keys
-    (i+1 causal, min(i+1, W) with a window, S without the causal mask) and O_i is their mean."""
-    S, D = 70, 4
-    q, k, v, do = _rng_inputs(24, 1, 2, 2, S, D)
-    q[:] = 0.0
-    for causal, window in ((True, 0), (True, 1), (True, 63), (True, 64), (True, 65), (False, 0)):
-        O, LSE = A.forward(q, k, v, causal, window, 1.0)
-        i = np.arange(S)
-        if not causal:
-            count = np.full(S, S)
-        elif window == 0:
-            count = i + 1
-        else:
-            count = np.minimum(i + 1, window)
-        assert np.array_equal(np.rint(np.exp(LSE[0, 0])).astype(np.int64), count), (causal, window)
+    (p+1 causal, min(p+1, W) with a window, S_k without the causal mask, where p = i + S_k - S_q
+    is the query's position) and O_i is their mean."""
+    D = 4
+    for S, Sk in ((70, 70), (20, 70), (1, 70)):
+        q, k, v, do = _rng_inputs(24, 1, 2, 2, S, D, Sk=Sk)
+        q[:] = 0.0
+        for causal, window in ((True, 0), (True, 1), (True, 63), (True, 64), (True, 65), (False, 0)):
+            O, LSE = A.forward(q, k, v, causal, window, 1.0)
+            p = np.arange(S) + Sk - S
+            if not causal:
+                count = np.full(S, Sk)
+            elif window == 0:
+                count = p + 1
+            else:
+                count = np.minimum(p + 1, window)
+            assert np.array_equal(np.rint(np.exp(LSE[0, 0])).astype(np.int64), count), (S, causal, window)
+            hi = p + 1 if causal else np.full(S, Sk)
+            lo = hi - count
+            for i in (0, S // 2, S - 1):
+                want = v[0, 0, lo[i]:hi[i]].mean(axis=0)
+                assert np.max(np.abs(O[0, 0, i] - want)) <= 1e-14, (S, causal, window, i)
 
 
 # ---------------------------------------------------------------- invariants
@@ -337,9 +354,94 @@ def pin_row_and_column_helpers(A):
         assert np.max(np.abs(dv - r["dV"][1, 1, cols])) <= 1e-13
 
 
+# ---------------------------------------------------------------- fewer queries than keys
+def pin_chunk_is_suffix_of_square(A):
+    """A chunk of the last S_q queries against all S_k keys is the square S_k x S_k problem seen
+    on its last S_q rows: O, LSE and dQ equal those rows, and dK / dV equal the square problem's
+    with dO zero on the first S_k - S_q rows (the other rows then contribute nothing)."""
+    Sk, D = 29, 8
+    qf, k, v, dof = _rng_inputs(31, 2, 4, 2, Sk, D)
+    for S in (29, 17, 8, 1):
+        for window in (0, 1, 6, 40):
+            q, do = qf[:, :, Sk - S:], dof[:, :, Sk - S:]
+            r = A.forward_backward(q, k, v, do, True, window, 0.45)
+            dz = dof.copy()
+            dz[:, :, :Sk - S] = 0.0
+            full = A.forward_backward(qf, k, v, dz, True, window, 0.45)
+            for name in ("O", "LSE", "dQ"):
+                err = np.max(np.abs(r[name] - full[name][:, :, Sk - S:]))
+                assert err <= 1e-13, f"chunk {name} (S_q={S}, W={window}): {err:.3e}"
+            for name in ("dK", "dV"):
+                err = np.max(np.abs(r[name] - full[name]))
+                assert err <= 1e-13, f"chunk {name} (S_q={S}, W={window}): {err:.3e}"
+
+
+def pin_torch_lower_right_causal(A, tol=1e-12):
+    """torch's own lower-right causal bias (torch.nn.attention.bias.causal_lower_right) with
+    float64 CPU scaled_dot_product_attention and autograd, for S_q < S_k without a window."""
+    import torch
+    from torch.nn.attention.bias import causal_lower_right
+    for (B, Hq, Hkv, S, Sk, D, seed) in ((1, 4, 2, 11, 30, 8, 32), (2, 2, 1, 1, 17, 4, 33)):
+        q, k, v, do = _rng_inputs(seed, B, Hq, Hkv, S, D, Sk=Sk)
+        scale = 1.0 / math.sqrt(D)
+        r = A.forward_backward(q, k, v, do, True, 0, scale)
+        G = Hq // Hkv
+        tq = torch.tensor(q, requires_grad=True)
+        tk = torch.tensor(k, requires_grad=True)
+        tv = torch.tensor(v, requires_grad=True)
+        mask = causal_lower_right(S, Sk)._materialize(torch.device("cpu"))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1),
+            attn_mask=mask, scale=scale)
+        o.backward(torch.tensor(do))
+        for name, x, y in (("O", r["O"], o.detach().numpy()), ("dQ", r["dQ"], tq.grad.numpy()),
+                           ("dK", r["dK"], tk.grad.numpy()), ("dV", r["dV"], tv.grad.numpy())):
+            err = np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30)
+            assert err <= tol, f"torch lower-right causal {name} (S_q={S}, S_k={Sk}): {err:.3e}"
+
+
+def pin_single_decode_query(A):
+    """One query against S_k keys stands at the last position: causally it sees every key, so it
+    equals attention without the causal mask; with a window W it equals attention over the last W
+    keys alone."""
+    Sk, D = 40, 8
+    q, k, v, do = _rng_inputs(34, 1, 4, 2, 1, D, Sk=Sk)
+    r = A.forward_backward(q, k, v, do, True, 0, 0.6)
+    nc = A.forward_backward(q, k, v, do, False, 0, 0.6)
+    for name in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.max(np.abs(r[name] - nc[name])) <= 1e-14, f"decode {name}"
+    for W in (1, 7, 39, 40, 64):
+        r = A.forward_backward(q, k, v, do, True, W, 0.6)
+        n = min(W, Sk)
+        sub = A.forward_backward(q, k[:, :, Sk - n:], v[:, :, Sk - n:], do, False, 0, 0.6)
+        for name in ("O", "LSE", "dQ"):
+            assert np.max(np.abs(r[name] - sub[name])) <= 1e-14, f"decode W={W} {name}"
+        for name in ("dK", "dV"):
+            assert np.max(np.abs(r[name][:, :, Sk - n:] - sub[name])) <= 1e-14, f"decode W={W} {name}"
+            assert np.all(r[name][:, :, :Sk - n] == 0.0), f"decode W={W} {name} outside the window"
+
+
+def pin_chunk_helpers(A):
+    """The row/column helpers agree with the full pass when S_q < S_k."""
+    q, k, v, do = _rng_inputs(35, 1, 4, 2, 21, 8, Sk=50)
+    for window in (0, 9):
+        r = A.forward_backward(q, k, v, do, True, window, 0.4, row_block=8)
+        rows = np.array([0, 3, 20])
+        O, LSE = A.rows_forward(q, k, v, 0, 2, rows, True, window, 0.4)
+        assert np.max(np.abs(O - r["O"][0, 2, rows])) <= 1e-14
+        assert np.max(np.abs(LSE - r["LSE"][0, 2, rows])) <= 1e-14
+        dq = A.rows_dq(q, k, v, do, 0, 2, rows, True, window, 0.4)
+        assert np.max(np.abs(dq - r["dQ"][0, 2, rows])) <= 1e-13
+        cols = np.array([0, 28, 29, 40, 49])
+        dk, dv = A.cols_dkdv(q, k, v, do, 0, 1, cols, True, window, 0.4, row_block=5)
+        assert np.max(np.abs(dk - r["dK"][0, 1, cols])) <= 1e-13
+        assert np.max(np.abs(dv - r["dV"][0, 1, cols])) <= 1e-13
+
+
 ALL_PINS = [
     pin_fd_every_entry, pin_bruteforce, pin_torch_sdpa, pin_three_token_closed_form,
     pin_constant_v, pin_identical_keys, pin_window_one, pin_zero_queries, pin_rows_sum_to_one,
     pin_gradient_identities, pin_gqa_is_repeated_mha, pin_hidden_keys_do_not_matter,
-    pin_row_and_column_helpers,
+    pin_row_and_column_helpers, pin_chunk_is_suffix_of_square, pin_torch_lower_right_causal,
+    pin_single_decode_query, pin_chunk_helpers,
 ]

@@ -14,8 +14,8 @@ _real_mask = A.visible_mask
 
 
 def _head_rows_mut(kind):
-    def f(qh, kh, vh, rows, causal, window, scale, doh=None):
-        t = _real_head_rows(qh, kh, vh, rows, causal, window, scale, doh)
+    def f(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0):
+        t = _real_head_rows(qh, kh, vh, rows, causal, window, scale, doh, offset)
         if doh is not None:
             if kind == "dropped_delta":          # dS = P * dP (rowsum term dropped)
                 t["dS"] = t["P"] * t["dP"]
@@ -47,8 +47,12 @@ def _fb_mut(kind):
 
 
 def _mask_mut(kind):
-    def f(rows, cols, causal, window):
-        i = np.asarray(rows, dtype=np.int64)[:, None]
+    def f(rows, cols, causal, window, offset=0):
+        if kind == "offset_ignored":          # queries aligned top-left instead of bottom-right
+            offset = 0
+        elif kind == "offset_negated":
+            offset = -offset
+        i = np.asarray(rows, dtype=np.int64)[:, None] + offset
         j = np.asarray(cols, dtype=np.int64)[None, :]
         m = np.ones((i.shape[0], j.shape[1]), dtype=bool)
         if causal:
@@ -70,6 +74,8 @@ MUTANTS = {
     "kv_head_interleaved": ("kv_head", lambda h, Hq, Hkv: h % Hkv),
     "window_off_by_one": ("visible_mask", _mask_mut("window_off_by_one")),
     "causal_transposed": ("visible_mask", _mask_mut("causal_transposed")),
+    "offset_ignored": ("visible_mask", _mask_mut("offset_ignored")),
+    "offset_negated": ("visible_mask", _mask_mut("offset_negated")),
 }
 
 # Pins that run quickly enough to try on every mutant.
