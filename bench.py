@@ -7,6 +7,9 @@ bf16, causal. Prints one JSON line.
 
 FLOPs are counted as 4*B*Hq*N*D for the forward, with N = S^2/2 attended pairs under the causal
 mask (the exact pair count with a window, S^2 without a mask), and 2.5x that for the backward.
+With fewer queries than keys (--workload naming a prefill-chunk or decode shape: Sq queries at
+the last Sq of S positions) N = (S^2 - (S-Sq)^2)/2 causal, the exact count with a window, Sq*S
+without a mask.
 """
 from __future__ import annotations
 
@@ -35,13 +38,19 @@ KERNEL_SOURCES = {
 }
 
 
-def attended_pairs(S: int, causal: bool, window: int) -> float:
+def attended_pairs(S: int, causal: bool, window: int, Sq: int | None = None) -> float:
+    """Attended (query, key) pairs for Sq queries at the last Sq of S key positions."""
+    Sq = S if Sq is None else Sq
+    off = S - Sq
     if not causal:
-        return float(S) * S
+        return float(Sq) * S
     if window == 0:
-        return S * S / 2.0
-    W = min(window, S)
-    return W * (W + 1) / 2.0 + (S - W) * W
+        return (float(S) * S - float(off) * off) / 2.0
+
+    def upto(n):  # sum over positions p < n of min(p + 1, W)
+        W = min(window, n)
+        return W * (W + 1) / 2.0 + (n - W) * window
+    return upto(S) - upto(off)
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -123,11 +132,11 @@ def cpu_baseline(w, q, k, v, do, heads: int):
     oracle.forward_backward(q[:, :heads], k[:, :groups], v[:, :groups], do[:, :heads],
                             w.causal, w.window, w.scale)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.B * heads * attended_pairs(w.S, w.causal, w.window) * w.D * 3.5
+    flops = 4.0 * w.B * heads * attended_pairs(w.S, w.causal, w.window, w.n_q) * w.D * 3.5
     model, blas = host_info()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle fwd+bwd on {heads} of {w.Hq} query heads ({groups} KV groups), "
-                      f"B={w.B}, S={w.S}, D={w.D}: {dt:.2f} s wall",
+                      f"B={w.B}, Sq={w.n_q}, S={w.S}, D={w.D}: {dt:.2f} s wall",
             "cpu_model": model, "blas": blas}
 
 
@@ -171,15 +180,25 @@ def main() -> int:
     q, k, v, do = make_inputs(w)
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     tq, tk, tv, tdo = (torch.from_numpy(x).to(td).cuda() for x in (q, k, v, do))
+    Sq = w.n_q
     o = torch.empty_like(tq)
-    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.Hq, Sq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
-    ws = torch.empty(fa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D), dtype=torch.uint8,
-                     device="cuda")
+    ws_bytes = fa.attn_bwd_qk_workspace_bytes(w.B, w.Hq, w.Hkv, Sq, w.S, w.D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    # the square workloads go through attn_fwd / attn_bwd, the others through the _qk entry points
+    fwd_call = fa.attn_fwd if Sq == w.S else fa.attn_fwd_qk
+    bwd_call = fa.attn_bwd if Sq == w.S else fa.attn_bwd_qk
+
+    def fwd():
+        fwd_call(tq, tk, tv, o, lse, w.causal, w.window, w.scale)
+
+    def bwd():
+        bwd_call(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window, w.scale)
 
     def step():
-        fa.attn_fwd(tq, tk, tv, o, lse, w.causal, w.window, w.scale)
-        fa.attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window, w.scale)
+        fwd()
+        bwd()
 
     for _ in range(args.warmup):
         step()
@@ -207,12 +226,8 @@ def main() -> int:
         ms = sorted(a.elapsed_time(b) for a, b in out)
         return {"median": round(ms[len(ms) // 2], 4), "min": round(ms[0], 4)}
 
-    phases = {
-        "fwd": timed(lambda: fa.attn_fwd(tq, tk, tv, o, lse, w.causal, w.window, w.scale), args.steps),
-        "bwd": timed(lambda: fa.attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window,
-                                         w.scale), args.steps),
-        "fwd+bwd": timed(step, args.steps),
-    }
+    phases = {"fwd": timed(fwd, args.steps), "bwd": timed(bwd, args.steps),
+              "fwd+bwd": timed(step, args.steps)}
 
     # per-kernel durations: HIP events recorded on the launch stream around each kernel
     events = {}
@@ -235,7 +250,7 @@ def main() -> int:
         d = [evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2)]
         kern_ms[name] = sum(d) / len(d)
 
-    N = attended_pairs(w.S, w.causal, w.window)
+    N = attended_pairs(w.S, w.causal, w.window, Sq)
     unit = 2.0 * w.B * w.Hq * N * w.D  # one GEMM-sized pass over the attended pairs
     fl = {"attn_fwd": 2 * unit, "attn_bwd_dkdv": 4 * unit, "attn_bwd_dq": 1 * unit}
     total_flops = 7 * unit  # forward (2) + backward counted as 2.5x forward (5)
@@ -243,10 +258,9 @@ def main() -> int:
     value = total_flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     eb = 2 if w.dtype == "bf16" else 4
-    delta_bytes = w.B * w.Hq * w.S * (2 * w.D * eb + 12)  # read O, dO, lse; write delta, lse2
+    delta_bytes = w.B * w.Hq * Sq * (2 * w.D * eb + 12)  # read O, dO, lse; write delta, lse2
     nkv = w.B * w.Hkv * w.S * w.D
-    ws_bytes = fa.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D)
-    parts = (ws_bytes - 2 * ((w.B * w.Hq * w.S * 4 + 255) // 256 * 256)) // (2 * nkv * 4)
+    parts = (ws_bytes - 2 * ((w.B * w.Hq * Sq * 4 + 255) // 256 * 256)) // (2 * nkv * 4)
     hbm_bytes = {"attn_bwd_delta": delta_bytes,
                  "attn_bwd_dkdv_reduce": 2 * nkv * (4 * max(parts, 1) + eb)}
 
@@ -275,7 +289,8 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
-                   "causal": w.causal, "window": w.window, "parallelism": "none (1 GPU)"},
+                   "causal": w.causal, "window": w.window, "parallelism": "none (1 GPU)",
+                   **({"Sq": Sq} if Sq != w.S else {})},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "phase_ms": phases,
         "phase_tflops_median": {

@@ -46,6 +46,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_qk.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_qk.restype = i
+    lib.attn_bwd_qk.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                i, i, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd_qk.restype = i
+    lib.attn_bwd_qk_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -89,6 +96,10 @@ def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, D: int) -> int:
     return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, S, D))
 
 
+def attn_bwd_qk_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int) -> int:
+    return int(load_library().attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D))
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -116,75 +127,115 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _fwd_args(q, k, v, o, lse, causal, window, scale):
+    import torch
+    if not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous GPU tensor")
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    _check_tensor("k", k, (B, Hkv, Sk, D), q.dtype, q.device)
+    _check_tensor("v", v, (B, Hkv, Sk, D), q.dtype, q.device)
+    _check_tensor("o", o, (B, Hq, Sq, D), q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, Sq), torch.float32, q.device)
+    scale = D ** -0.5 if scale is None else float(scale)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+    return ptrs, (B, Hq, Hkv, Sq, Sk, D), (int(bool(causal)), int(window), scale)
+
+
 def attn_fwd(q, k, v, o, lse, causal: bool = True, window: int = 0, scale: float | None = None,
              stream=None) -> None:
     """Calls attn_fwd: q [B,Hq,S,D], k/v [B,Hkv,S,D] -> o [B,Hq,S,D] (q's dtype), lse [B,Hq,S] f32."""
-    import torch
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    _check_tensor("k", k, (B, Hkv, S, D), q.dtype, q.device)
-    _check_tensor("v", v, (B, Hkv, S, D), q.dtype, q.device)
-    _check_tensor("o", o, (B, Hq, S, D), q.dtype, q.device)
-    _check_tensor("lse", lse, (B, Hq, S), torch.float32, q.device)
-    if not q.is_contiguous() or q.device.type != "cuda":
-        raise ValueError("q must be a contiguous GPU tensor")
-    scale = D ** -0.5 if scale is None else float(scale)
-    st = load_library().attn_fwd(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                 o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, S, D, int(bool(causal)),
-                                 int(window), scale, _stream(stream))
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), tail = _fwd_args(q, k, v, o, lse, causal, window, scale)
+    if Sq != Sk:
+        raise ValueError("attn_fwd takes as many queries as keys; use attn_fwd_qk")
+    st = load_library().attn_fwd(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, D, *tail, _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
+
+
+def attn_fwd_qk(q, k, v, o, lse, causal: bool = True, window: int = 0, scale: float | None = None,
+                stream=None) -> None:
+    """Calls attn_fwd_qk: q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] with Sq <= Sk (the queries are the last
+    Sq positions) -> o [B,Hq,Sq,D], lse [B,Hq,Sq] f32."""
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), tail = _fwd_args(q, k, v, o, lse, causal, window, scale)
+    st = load_library().attn_fwd_qk(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, Sk, D, *tail,
+                                    _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_qk")
+
+
+def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale):
+    import torch
+    if not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous GPU tensor")
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    for name, t, shp in (("k", k, (B, Hkv, Sk, D)), ("v", v, (B, Hkv, Sk, D)),
+                         ("o", o, (B, Hq, Sq, D)), ("dout", dout, (B, Hq, Sq, D)),
+                         ("dq", dq, (B, Hq, Sq, D)), ("dk", dk, (B, Hkv, Sk, D)),
+                         ("dv", dv, (B, Hkv, Sk, D))):
+        _check_tensor(name, t, shp, q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, Sq), torch.float32, q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    scale = D ** -0.5 if scale is None else float(scale)
+    nbytes = workspace.numel() * workspace.element_size()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), nbytes)
+    return ptrs, (B, Hq, Hkv, Sq, Sk, D), (int(bool(causal)), int(window), scale)
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = True, window: int = 0,
              scale: float | None = None, stream=None) -> None:
     """Calls attn_bwd; dq/dk/dv are overwritten. workspace: a uint8 GPU tensor of at least
     attn_bwd_workspace_bytes(...) bytes."""
-    import torch
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    for name, t, shp in (("k", k, (B, Hkv, S, D)), ("v", v, (B, Hkv, S, D)), ("o", o, (B, Hq, S, D)),
-                         ("dout", dout, (B, Hq, S, D)), ("dq", dq, (B, Hq, S, D)),
-                         ("dk", dk, (B, Hkv, S, D)), ("dv", dv, (B, Hkv, S, D))):
-        _check_tensor(name, t, shp, q.dtype, q.device)
-    _check_tensor("lse", lse, (B, Hq, S), torch.float32, q.device)
-    if not q.is_contiguous() or q.device.type != "cuda":
-        raise ValueError("q must be a contiguous GPU tensor")
-    if workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on q's device")
-    scale = D ** -0.5 if scale is None else float(scale)
-    nbytes = workspace.numel() * workspace.element_size()
-    st = load_library().attn_bwd(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                 o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
-                                 dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), nbytes,
-                                 B, Hq, Hkv, S, D, int(bool(causal)), int(window), scale,
-                                 _stream(stream))
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), tail = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                                                    causal, window, scale)
+    if Sq != Sk:
+        raise ValueError("attn_bwd takes as many queries as keys; use attn_bwd_qk")
+    st = load_library().attn_bwd(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, D, *tail, _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
 
 
+def attn_bwd_qk(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = True,
+                window: int = 0, scale: float | None = None, stream=None) -> None:
+    """Calls attn_bwd_qk (Sq <= Sk); dq/dk/dv are overwritten. workspace: a uint8 GPU tensor of
+    at least attn_bwd_qk_workspace_bytes(...) bytes."""
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), tail = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                                                    causal, window, scale)
+    st = load_library().attn_bwd_qk(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, Sk, D, *tail,
+                                    _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_qk")
+
+
 # ---------------------------------------------------------------- allocation conveniences
 def forward(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None, stream=None):
-    """Allocates o and lse with torch, then calls attn_fwd. Returns (o, lse)."""
+    """Allocates o and lse with torch, then calls attn_fwd (attn_fwd_qk when k has more rows than
+    q). Returns (o, lse)."""
     import torch
-    B, Hq, S, D = q.shape
+    B, Hq, Sq, D = q.shape
     o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, causal, window, scale, stream)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    call = attn_fwd if k.shape[2] == Sq else attn_fwd_qk
+    call(q, k, v, o, lse, causal, window, scale, stream)
     return o, lse
 
 
 def backward(q, k, v, o, lse, dout, causal: bool = True, window: int = 0,
              scale: float | None = None, stream=None, workspace=None):
-    """Allocates dq, dk, dv (and the workspace if none is given), then calls attn_bwd."""
+    """Allocates dq, dk, dv (and the workspace if none is given), then calls attn_bwd
+    (attn_bwd_qk when k has more rows than q)."""
     import torch
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
     if workspace is None:
-        workspace = torch.empty(max(1, attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)),
+        workspace = torch.empty(max(1, attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)),
                                 dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale, stream)
+    call = attn_bwd if Sk == Sq else attn_bwd_qk
+    call(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale, stream)
     return dq, dk, dv

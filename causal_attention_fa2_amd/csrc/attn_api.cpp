@@ -5,7 +5,9 @@
 // (query heads split into equal contiguous groups, Grip paragraph of the "KYNETRA FOUNDRY" page);
 // window 0 means no window and a window needs the causal mask (the single window parameter of
 // "CUDA-LLM: A GitHub Repository for Development", section "The custom CUDA kernel", only ever
-// narrows causal attention).
+// narrows causal attention); with fewer queries than keys the queries are the last Sq positions
+// (same section: one kernel for prefill and for one-token decode against a cache), and more
+// queries than keys is not defined.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -19,9 +21,9 @@ namespace {
 attn_launch_hook_t g_hook = nullptr;
 void* g_hook_user = nullptr;
 
-int check_common(int dtype, int B, int Hq, int Hkv, int S, int D, int causal, int window,
-                 float scale) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || D <= 0) return ATTN_ERR_INVALID;
+int check_common(int dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                 int window, float scale) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || D <= 0) return ATTN_ERR_INVALID;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
   if (window < 0) return ATTN_ERR_INVALID;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
@@ -29,8 +31,9 @@ int check_common(int dtype, int B, int Hq, int Hkv, int S, int D, int causal, in
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
   if (!causal && window > 0) return ATTN_ERR_UNSUPPORTED;
-  const int64_t elems = (int64_t)B * Hq * S * D;
-  if (elems >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (Sq > Sk) return ATTN_ERR_UNSUPPORTED;  // the queries are the last Sq of Sk positions
+  const int64_t q_elems = (int64_t)B * Hq * Sq * D, kv_elems = (int64_t)B * Hkv * Sk * D;
+  if (q_elems >= ((int64_t)1 << 31) || kv_elems >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -51,10 +54,11 @@ void attn_set_launch_hook(attn_launch_hook_t hook, void* user) {
 }
 
 
-int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
-             int Hq, int Hkv, int S, int D, int causal, int window, float scale, void* stream) {
+int attn_fwd_qk(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, float scale,
+                void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
-  int st = check_common(dtype, B, Hq, Hkv, S, D, causal, window, scale);
+  int st = check_common(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
   if (st != ATTN_OK) return st;
   fa::Args a{};
   a.dtype = dtype;
@@ -66,7 +70,8 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.S = S;
+  a.Sq = Sq;
+  a.Sk = Sk;
   a.D = D;
   a.causal = causal;
   a.window = window;
@@ -75,20 +80,29 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
   return fa::launch_fwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
-size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
-  if (check_common(ATTN_BF16, B, Hq, Hkv, S, D, 1, 0, 1.0f) != ATTN_OK) return 0;
-  return fa::bwd_workspace_bytes(B, Hq, Hkv, S, D);
+int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+             int Hq, int Hkv, int S, int D, int causal, int window, float scale, void* stream) {
+  return attn_fwd_qk(dtype, q, k, v, o, lse, B, Hq, Hkv, S, S, D, causal, window, scale, stream);
 }
 
-int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
-             const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
-             size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int causal, int window,
-             float scale, void* stream) {
+size_t attn_bwd_qk_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
+  if (check_common(ATTN_BF16, B, Hq, Hkv, Sq, Sk, D, 1, 0, 1.0f) != ATTN_OK) return 0;
+  return fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D);
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
+  return attn_bwd_qk_workspace_bytes(B, Hq, Hkv, S, S, D);
+}
+
+int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const void* o,
+                const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                int window, float scale, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return ATTN_ERR_INVALID;
-  int st = check_common(dtype, B, Hq, Hkv, S, D, causal, window, scale);
+  int st = check_common(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
   if (st != ATTN_OK) return st;
-  if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, Hkv, S, D)) return ATTN_ERR_INVALID;
+  if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)) return ATTN_ERR_INVALID;
   fa::Args a{};
   a.dtype = dtype;
   a.q = q;
@@ -100,20 +114,29 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  const size_t row_bytes = fa::delta_bytes(B, Hq, S);
+  const size_t row_bytes = fa::delta_bytes(B, Hq, Sq);
   a.delta = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + row_bytes);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_bytes);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.S = S;
+  a.Sq = Sq;
+  a.Sk = Sk;
   a.D = D;
   a.causal = causal;
   a.window = window;
   a.scale = scale;
   a.stream = stream;
   return fa::launch_bwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int causal, int window,
+             float scale, void* stream) {
+  return attn_bwd_qk(dtype, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq,
+                     Hkv, S, S, D, causal, window, scale, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dQ,
-    int B, int Hq, int Hkv, int S, int causal, int window, float scale, float scale_log2, int n_qt) {
+    int B, int Hq, int Hkv, int Sq, int S, int causal, int window, float scale, float scale_log2,
+    int n_qt) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 32 * KB;
   constexpr int DS = D / 16;
@@ -93,17 +94,20 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   const int qt = causal ? n_qt - 1 - rank : rank;
   const int b = bg / Hkv;
   const int h = (bg - b * Hkv) * G + hh;
-  const size_t q_off = (size_t)(b * Hq + h) * S * D;
+  const int off = S - Sq;  // query row r stands at key position r + off
+  const size_t q_off = (size_t)(b * Hq + h) * Sq * D;
   const typename E::T* k_bg = K + (size_t)bg * S * D;
   const typename E::T* v_bg = V + (size_t)bg * S * D;
 
   const int q0 = qt * BR;
   const int qw = q0 + 32 * w;
   const int my_q = qw + l32;
-  const bool q_ok = my_q < S;
+  const bool q_ok = my_q < Sq;
+  const int pw = qw + off;  // positions of this wave's rows
+  const int my_p = my_q + off;
 
   int jt_lo, jt_hi;
-  kv_tile_range(q0, imin_(q0 + BR - 1, S - 1), S, BC, causal, window, &jt_lo, &jt_hi);
+  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, &jt_lo, &jt_hi);
   const int n_steps = jt_hi - jt_lo + 1;
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
     const int j0 = (jt_lo + s) * BC;
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     qf[s] = load_frag_global(Q + q_off + (size_t)my_q * D + 16 * s + 8 * half, q_ok);
     df[s] = load_frag_global(dO + q_off + (size_t)my_q * D + 16 * s + 8 * half, q_ok);
   }
-  const size_t row_idx = (size_t)(b * Hq + h) * S + (q_ok ? my_q : 0);
+  const size_t row_idx = (size_t)(b * Hq + h) * Sq + (q_ok ? my_q : 0);
   const float nlse2 = -LSE2[row_idx];
   const float dl = delta[row_idx];
   f32x16_t acc[DB];
@@ -130,8 +134,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
     const char* v_lds = k_lds + KvTile::kBytes;
     const int j0 = (jt_lo + s) * BC;
-    if (block_empty(qw, qw + 31, j0, j0 + BC - 1, S, causal, window)) return;
-    const bool full = block_full(qw, qw + 31, j0, j0 + BC - 1, S, causal, window);
+    if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window)) return;
+    const bool full = block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16_t st = f32x16_t{}, dpt = f32x16_t{};
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(fmaf(st[r], scale_log2, nlse2));
           if constexpr (decltype(maskc)::value) {
-            if (!visible(my_q, j0 + 32 * kb + acc_row(r), S, causal, window)) p = 0.f;
+            if (!visible(my_p, j0 + 32 * kb + acc_row(r), S, causal, window)) p = 0.f;
           }
           st[r] = p * (dpt[r] - dl);
         }
@@ -201,7 +205,7 @@ static int launch_bwd_t(const Args& a) {
   typedef typename E::T T;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   {
-    const int rows = a.B * a.Hq * a.S;
+    const int rows = a.B * a.Hq * a.Sq;
     constexpr int RPB = 256 / (D / 8);
     dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
     notify_launch("attn_bwd_delta", 0, a.stream);
@@ -213,12 +217,13 @@ static int launch_bwd_t(const Args& a) {
   {
     constexpr int NW = E::kBytes == 2 ? 8 : 4;
     constexpr int KB = E::kBytes == 2 ? 2 : 1;
-    const int n_qt = (a.S + 32 * NW - 1) / (32 * NW);
+    const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
     dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
     notify_launch("attn_bwd_dq", 0, a.stream);
     hipLaunchKernelGGL((dq_kernel<E, D, NW, KB>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
-                       (T*)a.dq, a.B, a.Hq, a.Hkv, a.S, a.causal, a.window, a.scale, scale_log2, n_qt);
+                       (T*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.scale, scale_log2,
+                       n_qt);
     notify_launch("attn_bwd_dq", 1, a.stream);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

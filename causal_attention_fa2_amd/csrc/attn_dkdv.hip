@@ -16,8 +16,8 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dK,
-    typename E::T* __restrict__ dV, float* __restrict__ part, int B, int Hq, int Hkv, int S,
-    int causal, int window, float scale, float scale_log2, int n_kt, int n_pairs, int hs) {
+    typename E::T* __restrict__ dV, float* __restrict__ part, int B, int Hq, int Hkv, int Sq,
+    int S, int causal, int window, float scale, float scale_log2, int n_kt, int n_pairs, int hs) {
   constexpr int BC = 32 * NW;  // keys per workgroup
   constexpr int BR = 32 * QB;  // query rows per streamed tile
   constexpr int DS = D / 16;
@@ -52,14 +52,15 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   const int tb = n_kt - 1 - pair;
   const bool two = tb > ta;
   const size_t kv_off = (size_t)bg * S * D;
+  const int qoff = S - Sq;  // query row r stands at key position r + qoff
 
   // Segment = one key tile: the workgroup runs key tile ta, then key tile tb.
   int kt = ta, lo = 0, nq = 0, n_steps = 0;
   auto set_segment = [&](int t) __attribute__((always_inline)) {
     int hi;
     kt = t;
-    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, BR, causal, window, &lo, &hi);
-    nq = hi - lo + 1;
+    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, &lo, &hi);
+    nq = imax_(hi - lo + 1, 0);  // 0: no query sees these keys, so dK = dV = 0
     n_steps = hpg * nq;
   };
   // step -> (query head, first query row) of the current segment
@@ -69,10 +70,10 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   auto issue = [&](int hh, int it, char* stg) __attribute__((always_inline)) {
     const int i0 = (lo + nq - 1 - it) * BR;
     const size_t bh = (size_t)b * Hq + h0 + hh;
-    dma_tile<E, BR, D, NW>(stg, Q + bh * S * D, i0, S);
-    dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * S * D, i0, S);
-    if (w == 0) dma_row_floats(stg + kRowOff, LSE2 + bh * S, i0, S);
-    if (w == 1) dma_row_floats(stg + kRowOff + 256, delta + bh * S, i0, S);
+    dma_tile<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, Sq);
+    dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, Sq);
+    if (w == 0) dma_row_floats(stg + kRowOff, LSE2 + bh * Sq, i0, Sq);
+    if (w == 1) dma_row_floats(stg + kRowOff + 256, delta + bh * Sq, i0, Sq);
   };
   auto advance = [&](int& hh, int& it) __attribute__((always_inline)) {
     if (++it == nq) {
@@ -127,11 +128,12 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
     const float* dl_lds = lse_lds + 64;
     const int i0 = (lo + nq - 1 - it) * BR;
+    const int p0 = i0 + qoff;  // position of the tile's first row
     const int kw = kt * BC + 32 * w;
     const int my_k = kw + l32;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int r0 = i0 + 32 * qb;
+      const int r0 = p0 + 32 * qb;
       if (block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window)) continue;
       const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window);
       // All Q / dO row fragments of this block in flight before the S / dP products, so the
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
             const int r = 4 * r4 + c;
             float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse4[c]));
             if constexpr (decltype(maskc)::value) {
-              if (!visible(i0 + rb + c, my_k, S, causal, window)) p = 0.f;
+              if (!visible(p0 + rb + c, my_k, S, causal, window)) p = 0.f;
             }
             sa[r] = p;
             dp[r] = p * (dp[r] - dl4[c]);
@@ -234,8 +236,10 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     set_segment(seg ? tb : ta);
     load_kv();
     ch = 0, ct = 0, ih = 0, iq = 0;
-    issue(ih, iq, st0);
-    advance(ih, iq);
+    if (n_steps > 0) {
+      issue(ih, iq, st0);
+      advance(ih, iq);
+    }
     if (n_steps > 1) {
       issue(ih, iq, st1);
       advance(ih, iq);
@@ -281,16 +285,16 @@ static int launch_dkdv_t(const Args& a) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     constexpr int NW = kDkdvWaves;
     constexpr int QB = E::kBytes == 2 ? 2 : 1;
-    const DkdvPlan p = dkdv_plan(a.B, a.Hq, a.Hkv, a.S);
+    const DkdvPlan p = dkdv_plan(a.B, a.Hq, a.Hkv, a.Sk);
     dim3 grid((unsigned)(p.n_pairs * a.B * a.Hkv * p.hs)), block(NW * 64);
     notify_launch("attn_bwd_dkdv", 0, a.stream);
     hipLaunchKernelGGL((dkdv_kernel<E, D, NW, QB>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
-                       (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.S, a.causal, a.window, a.scale,
-                       scale_log2, p.n_kt, p.n_pairs, p.hs);
+                       (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window,
+                       a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
     notify_launch("attn_bwd_dkdv", 1, a.stream);
     if (p.hs > 1) {
-      const size_t n = (size_t)a.B * a.Hkv * a.S * D;
+      const size_t n = (size_t)a.B * a.Hkv * a.Sk * D;
       dim3 rgrid((unsigned)((n / 4 + 255) / 256)), rblock(256);
       notify_launch("attn_bwd_dkdv_reduce", 0, a.stream);
       hipLaunchKernelGGL((dkdv_reduce_kernel<E>), rgrid, rblock, 0, st, (const float*)a.part,

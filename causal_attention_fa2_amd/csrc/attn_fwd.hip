@@ -30,7 +30,7 @@ template <class E, int D, int NW, int KB, int NST>
 __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
-    int B, int Hq, int Hkv, int S, int causal, int window, float scale_log2, int n_qt) {
+    int B, int Hq, int Hkv, int Sq, int S, int causal, int window, float scale_log2, int n_qt) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 32 * KB;
   constexpr int DS = D / 16;  // 16-wide contraction steps over the head dimension
@@ -57,17 +57,20 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   const int g = bg - b * Hkv;
   const int h = g * G + hh;
 
-  const typename E::T* q_bh = Q + (size_t)(b * Hq + h) * S * D;
+  const int off = S - Sq;  // query row r stands at key position r + off
+  const typename E::T* q_bh = Q + (size_t)(b * Hq + h) * Sq * D;
   const typename E::T* k_bg = K + (size_t)bg * S * D;
   const typename E::T* v_bg = V + (size_t)bg * S * D;
 
   const int q0 = qt * BR;
   const int qw = q0 + 32 * w;  // first row of this wave
   const int my_q = qw + l32;   // the query row this lane owns
-  const bool q_ok = my_q < S;
+  const bool q_ok = my_q < Sq;
+  const int pw = qw + off;     // positions of this wave's rows: pw .. pw + 31
+  const int my_p = my_q + off;
 
   int jt_lo, jt_hi;
-  kv_tile_range(q0, imin_(q0 + BR - 1, S - 1), S, BC, causal, window, &jt_lo, &jt_hi);
+  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, &jt_lo, &jt_hi);
   const int n_steps = jt_hi - jt_lo + 1;
 
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (!visible(my_q, j0 + 32 * kb + acc_row(r), S, causal, window)) st[kb][r] = kNegInf;
+          if (!visible(my_p, j0 + 32 * kb + acc_row(r), S, causal, window)) st[kb][r] = kNegInf;
           mx = fmaxf(mx, st[kb][r]);
         }
       }
@@ -176,15 +179,15 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
 
   auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
     const int j0 = (jt_lo + s) * BC;
-    if (block_empty(qw, qw + 31, j0, j0 + BC - 1, S, causal, window)) return;
-    compute_general(j0, k_lds, block_full(qw, qw + 31, j0, j0 + BC - 1, S, causal, window));
+    if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window)) return;
+    compute_general(j0, k_lds, block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window));
   };
 
   ring_run<NST, kStage, kOps>(ring, n_steps, issue, compute);
 
   if (!q_ok) return;
   const float inv_l = 1.f / l;
-  typename E::T* o_row = O + ((size_t)(b * Hq + h) * S + my_q) * D;
+  typename E::T* o_row = O + ((size_t)(b * Hq + h) * Sq + my_q) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
       }
     }
   }
-  if (half == 0) LSE[(size_t)(b * Hq + h) * S + my_q] = (m + __log2f(l)) * kLn2;
+  if (half == 0) LSE[(size_t)(b * Hq + h) * Sq + my_q] = (m + __log2f(l)) * kLn2;
 }
 
 template <class E, int D>
@@ -207,12 +210,12 @@ static int launch_fwd_t(const Args& a) {
   constexpr int NW = E::kBytes == 2 ? kFwdWaves : 4;
   constexpr int KB = E::kBytes == 2 ? 2 : 1;
   constexpr int NST = E::kBytes == 2 ? kFwdStages : 3;
-  const int n_qt = (a.S + 32 * NW - 1) / (32 * NW);
+  const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
   dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
   notify_launch("attn_fwd", 0, a.stream);
   hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NST>), grid, block, 0, (hipStream_t)a.stream,
                      (const typename E::T*)a.q, (const typename E::T*)a.k, (const typename E::T*)a.v,
-                     (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.causal, a.window,
+                     (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window,
                      (float)((double)a.scale * 1.4426950408889634), n_qt);
   notify_launch("attn_fwd", 1, a.stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -20,10 +20,10 @@ struct Args {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;       // backward workspace: rowsum(dO * O), [B, Hq, S]
-  float* lse2;        // backward workspace: lse * log2(e), [B, Hq, S]
+  float* delta;       // backward workspace: rowsum(dO * O), [B, Hq, Sq]
+  float* lse2;        // backward workspace: lse * log2(e), [B, Hq, Sq]
   float* part;        // backward workspace: fp32 dK / dV partial sums of the head-group parts
-  int B, Hq, Hkv, S, D;
+  int B, Hq, Hkv, Sq, Sk, D;  // Sq query rows, Sk >= Sq keys (queries: the last Sq positions)
   int causal, window;
   float scale;
   void* stream;
@@ -57,9 +57,9 @@ constexpr int kDkdvMinGroups = 256;
 struct DkdvPlan {
   int n_kt, n_pairs, hs;
 };
-inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int S) {
+inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int Sk) {
   DkdvPlan p;
-  p.n_kt = (S + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
+  p.n_kt = (Sk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
   p.n_pairs = (p.n_kt + 1) / 2;
   const long items = (long)B * Hkv * p.n_pairs;
   const int G = Hq / Hkv;
@@ -68,14 +68,14 @@ inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int S) {
   return p;
 }
 
-inline size_t delta_bytes(int B, int Hq, int S) {
-  return ((size_t)B * Hq * S * sizeof(float) + 255) / 256 * 256;
+inline size_t delta_bytes(int B, int Hq, int Sq) {
+  return ((size_t)B * Hq * Sq * sizeof(float) + 255) / 256 * 256;
 }
-// Workspace layout: delta [B,Hq,S] f32 | lse * log2(e) [B,Hq,S] f32 | dK/dV partials (if split).
-inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
-  const DkdvPlan p = dkdv_plan(B, Hq, Hkv, S);
-  size_t partials = p.hs > 1 ? (size_t)p.hs * 2 * B * Hkv * S * D * sizeof(float) : 0;
-  return 2 * delta_bytes(B, Hq, S) + partials;
+// Workspace layout: delta [B,Hq,Sq] f32 | lse * log2(e) [B,Hq,Sq] f32 | dK/dV partials (if split).
+inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
+  const DkdvPlan p = dkdv_plan(B, Hq, Hkv, Sk);
+  size_t partials = p.hs > 1 ? (size_t)p.hs * 2 * B * Hkv * Sk * D * sizeof(float) : 0;
+  return 2 * delta_bytes(B, Hq, Sq) + partials;
 }
 
 }  // namespace fa

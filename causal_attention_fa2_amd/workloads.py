@@ -14,9 +14,12 @@ measured and checked on; no dataset is involved, every input is synthetic):
   swa-w1024-s8192        B=1, Hq=Hkv=16, S=8192,  D=64,  bf16, causal, window 1024
   gqa64x8-s32768-d128    B=1, Hq=64, Hkv=8, S=32768, D=128, bf16, causal, Q and K
                          multiplied per head by factors drawn U(0.5, 2)
+  gqa64x8-q1024-k4096-d128  a prefill chunk: the last 1024 of 4096 positions (Sq=1024 queries,
+                         Sk=4096 keys), otherwise as gqa64x8-s4096-d128
+  gqa64x8-q1-k4096-d128  one decode query against 4096 cached keys, otherwise as above
 
 Draw order per workload: numpy.random.default_rng(seed); Q, K, V, dO as float32
-standard normals in that order (dO then scaled by its standard deviation); then, for the
+standard normals in that order (Q and dO with Sq rows, K and V with S rows) (dO then scaled by its standard deviation); then, for the
 long-context workload only, one factor per query head and one per KV head. Every tensor
 is then rounded once to the element type (round-to-nearest-even for bf16).
 """
@@ -42,13 +45,18 @@ class Workload:
     seed: int
     do_std: float = 1.0
     head_factor: bool = False  # multiply Q and K per head by U(0.5, 2) factors
+    Sq: int = 0  # query rows when fewer than the S keys (the last Sq positions); 0 = S
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.D)
 
+    @property
+    def n_q(self) -> int:
+        return self.Sq or self.S
+
     def shapes(self):
-        return ((self.B, self.Hq, self.S, self.D), (self.B, self.Hkv, self.S, self.D))
+        return ((self.B, self.Hq, self.n_q, self.D), (self.B, self.Hkv, self.S, self.D))
 
 
 WORKLOADS = {
@@ -60,6 +68,10 @@ WORKLOADS = {
         Workload("swa-w1024-s8192", 1, 16, 16, 8192, 64, "bf16", True, 1024, 1004),
         Workload("gqa64x8-s32768-d128", 1, 64, 8, 32768, 128, "bf16", True, 0, 1005,
                  head_factor=True),
+        Workload("gqa64x8-q1024-k4096-d128", 1, 64, 8, 4096, 128, "bf16", True, 0, 1006,
+                 do_std=0.1, Sq=1024),
+        Workload("gqa64x8-q1-k4096-d128", 1, 64, 8, 4096, 128, "bf16", True, 0, 1007,
+                 do_std=0.1, Sq=1),
     )
 }
 
@@ -94,17 +106,19 @@ def make_inputs(w: Workload, *, seed: int | None = None, B: int | None = None,
     """Draw (q, k, v, do) for workload `w` (optionally overriding its shape or seed).
 
     Returns float32 numpy arrays holding element-type-representable values:
-    q, do [B,Hq,S,D]; k, v [B,Hkv,S,D], all contiguous with D fastest."""
+    q, do [B,Hq,Sq,D]; k, v [B,Hkv,S,D], all contiguous with D fastest (Sq = S unless the
+    workload has fewer queries than keys)."""
     B = w.B if B is None else B
     Hq = w.Hq if Hq is None else Hq
     Hkv = w.Hkv if Hkv is None else Hkv
     S = w.S if S is None else S
     D = w.D if D is None else D
+    Sq = min(w.Sq, S) if w.Sq else S
     rng = np.random.default_rng(w.seed if seed is None else seed)
-    q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    q = rng.standard_normal((B, Hq, Sq, D), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
-    do = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    do = rng.standard_normal((B, Hq, Sq, D), dtype=np.float32)
     if w.do_std != 1.0:
         do *= np.float32(w.do_std)
     if w.head_factor:

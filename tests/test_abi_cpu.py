@@ -30,8 +30,9 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd",
-                     "attn_set_launch_hook", "attn_status_string"]
+    assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_qk", "attn_bwd_qk_workspace_bytes",
+                     "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_qk", "attn_set_launch_hook",
+                     "attn_status_string"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (attn_\w+)", out))
@@ -41,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fa.attn_abi_version() == 1
+    assert fa.attn_abi_version() == 2
     assert fa.attn_status_string(0) == "ok"
     assert fa.attn_status_string(1) == "invalid argument"
     assert fa.attn_status_string(2) == "unsupported configuration"
@@ -71,6 +72,22 @@ def test_workspace_bytes(lib):
     assert fa.attn_bwd_workspace_bytes(1, 2, 2, 3, 64) == 512  # two row arrays, 256-byte aligned
     assert fa.attn_bwd_workspace_bytes(1, 3, 2, 64, 64) == 0   # Hq % Hkv != 0
     assert fa.attn_bwd_workspace_bytes(1, 2, 2, 64, 96) == 0   # unsupported D
+
+
+def test_qk_workspace_bytes(lib):
+    """Row arrays follow the queries, partial sums (split head groups) follow the keys."""
+    for B, Hq, Hkv, Sq, Sk, D in ((1, 64, 8, 1024, 4096, 128), (1, 64, 8, 1, 4096, 128),
+                                  (2, 8, 2, 100, 300, 64), (1, 4, 4, 7, 7, 64), (1, 64, 8, 4096, 4096, 128)):
+        hs = _parts(B, Hq, Hkv, Sk)
+        rows = (B * Hq * Sq * 4 + 255) // 256 * 256
+        part = 2 * hs * B * Hkv * Sk * D * 4 if hs > 1 else 0
+        assert fa.attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) == 2 * rows + part
+        if Sq == Sk:
+            assert fa.attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) == \
+                fa.attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, D)
+    assert fa.attn_bwd_qk_workspace_bytes(1, 2, 2, 65, 64, 64) == 0  # more queries than keys
+    assert fa.attn_bwd_qk_workspace_bytes(1, 2, 2, 0, 64, 64) == 0
+    assert fa.attn_bwd_qk_workspace_bytes(1, 2, 2, 64, 0, 64) == 0
 
 
 P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
@@ -116,6 +133,43 @@ def test_bwd_validation(lib):
     assert bwd(lib, need, Hq=4, Hkv=3) == INV
     assert bwd(lib, need, D=32) == UNS
     assert bwd(lib, need, causal=0, window=1) == UNS
+
+
+def fwd_qk(lib, dtype=1, ptrs=(P, P, P, P, P), B=1, Hq=2, Hkv=2, Sq=16, Sk=64, D=64, causal=1,
+           window=0, scale=0.125):
+    return lib.attn_fwd_qk(dtype, *ptrs, B, Hq, Hkv, Sq, Sk, D, causal, window, scale, None)
+
+
+def bwd_qk(lib, ws_bytes=0, ptrs=(P,) * 10, B=1, Hq=2, Hkv=2, Sq=16, Sk=64, D=64, causal=1,
+           window=0, scale=0.125, dtype=1):
+    return lib.attn_bwd_qk(dtype, *ptrs, ws_bytes, B, Hq, Hkv, Sq, Sk, D, causal, window, scale,
+                           None)
+
+
+def test_qk_validation(lib):
+    INV, UNS = fa.ATTN_ERR_INVALID, fa.ATTN_ERR_UNSUPPORTED
+    for i in range(5):
+        ptrs = [P] * 5
+        ptrs[i] = None
+        assert fwd_qk(lib, ptrs=ptrs) == INV
+    assert fwd_qk(lib, Sq=0) == INV
+    assert fwd_qk(lib, Sk=0) == INV
+    assert fwd_qk(lib, Sq=65, Sk=64) == UNS        # more queries than keys is not defined
+    assert fwd_qk(lib, Hq=3, Hkv=2) == INV
+    assert fwd_qk(lib, causal=0, window=4) == UNS
+    assert fwd_qk(lib, D=96) == UNS
+    # each tensor below 2^31 elements: K/V [1, 8, 2^21, 128] is exactly 2^31
+    assert fwd_qk(lib, B=1, Hq=64, Hkv=8, Sq=1, Sk=1 << 21, D=128) == UNS
+    assert fwd_qk(lib, B=1, Hq=64, Hkv=8, Sq=1 << 18, Sk=1 << 18, D=128) == UNS
+    need = fa.attn_bwd_qk_workspace_bytes(1, 2, 2, 16, 64, 64)
+    assert need > 0
+    for i in range(10):
+        ptrs = [P] * 10
+        ptrs[i] = None
+        assert bwd_qk(lib, need, ptrs=ptrs) == INV
+    assert bwd_qk(lib, need - 1) == INV
+    assert bwd_qk(lib, need, Sq=65) == UNS
+    assert bwd_qk(lib, need, D=32) == UNS
 
 
 def test_launch_hook_set_and_clear(lib):

@@ -21,17 +21,20 @@ def driver(tmp_path_factory):
 
 
 S_LIST = [1, 2, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 255, 256, 257, 300]
+# fewer queries than keys: (S_q, S_k)
+QK_LIST = [(1, 2), (1, 100), (1, 257), (5, 300), (31, 64), (33, 200), (64, 65), (100, 129),
+           (127, 300), (128, 256), (200, 257), (255, 300)]
 W_LIST = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 1024]
 TILES = [32, 64, 128]
 
 
 def _configs():
-    for S in S_LIST:
+    for sq, sk in [(S, S) for S in S_LIST] + QK_LIST:
         for br in TILES:
             for bc in TILES:
-                yield (S, br, bc, 0, 0)
+                yield (sq, sk, br, bc, 0, 0)
                 for W in W_LIST:
-                    yield (S, br, bc, 1, W)
+                    yield (sq, sk, br, bc, 1, W)
 
 
 def test_tile_classifier_matches_mask(driver):
@@ -41,17 +44,17 @@ def test_tile_classifier_matches_mask(driver):
     lines = iter(out.splitlines())
     checked = 0
     for cfg in cfgs:
-        S, br, bc, causal, W = cfg
+        Sq, Sk, br, bc, causal, W = cfg
         assert next(lines) == "CFG " + " ".join(map(str, cfg))
-        nq, nk = -(-S // br), -(-S // bc)
-        m = oracle.visible_mask(np.arange(S), np.arange(S), bool(causal), W)
+        nq, nk = -(-Sq // br), -(-Sk // bc)
+        m = oracle.visible_mask(np.arange(Sq), np.arange(Sk), bool(causal), W, Sk - Sq)
         # pad to whole tiles: out-of-range rows / keys are never visible
         P = np.zeros((nq * br, nk * bc), bool)
-        P[:S, :S] = m
+        P[:Sq, :Sk] = m
         blocks = P.reshape(nq, br, nk, bc)
         any_vis = blocks.any(axis=(1, 3))
         inb = np.zeros((nq * br, nk * bc), bool)
-        inb[:S, :S] = True
+        inb[:Sq, :Sk] = True
         all_vis = (blocks & inb.reshape(nq, br, nk, bc)).all(axis=(1, 3)) & \
             inb.reshape(nq, br, nk, bc).all(axis=(1, 3)) & blocks.all(axis=(1, 3))
         for qt in range(nq):
@@ -64,8 +67,15 @@ def test_tile_classifier_matches_mask(driver):
             tag, kk, lo, hi = next(lines).split()
             assert (tag, int(kk)) == ("C", kt)
             rows = np.nonzero(any_vis[:, kt])[0]
+            if rows.size == 0:  # keys no query sees (they fall out of every window)
+                assert int(lo) > int(hi), (cfg, kt)
+                continue
             assert (int(lo), int(hi)) == (rows.min(), rows.max()), (cfg, kt)
             assert np.all(any_vis[rows.min():rows.max() + 1, kt]), (cfg, kt)
+        vis = next(lines)
+        assert vis[:2] == "V "
+        got = np.frombuffer(vis[2:].encode(), dtype=np.uint8).reshape(Sq, Sk) == ord("1")
+        assert np.array_equal(got, m), cfg
         classes = next(lines).split()[1] if nq * nk else ""
         want = np.where(~any_vis, "E", np.where(all_vis, "F", "P")).reshape(-1)
         assert classes == "".join(want), cfg
