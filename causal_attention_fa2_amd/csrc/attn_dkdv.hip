@@ -254,6 +254,248 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   }
 }
 
+// Split-role dK/dV kernel for bf16: the same decomposition as dkdv_kernel (a workgroup owns 128
+// keys of one KV head and streams the head group's query tiles through a 3-stage LDS-DMA ring),
+// but with 8 waves, two per SIMD. Waves w and w + 4 run on the same SIMD and own the same 32 keys:
+//   wave w     (S role):  S = Q K^T, P = exp2(S * scale * log2 e - lse * log2 e), dV += P^T dO
+//   wave w + 4 (dP role): dP = dO V^T, dS = P o (dP - delta), dK += dS^T Q
+// P passes from the S wave to its partner through LDS as bf16 in accumulator layout (2 KB per
+// 32 x 32 block). Each step (one 64-row query tile) has two workgroup barriers: the ring barrier
+// (the tile has landed; every wave is done with the previous step, including its P blocks) and one
+// after the products S and dP (the P blocks are written). Around the second barrier each wave's
+// vector work (exponentials, dS) can run while its partner issues matrix products on the shared
+// SIMD. Per wave: its K or V fragments (B operand), its dV or dK accumulators and the two blocks'
+// S / dP accumulators -- the two roles' state shares the same registers.
+template <int D, int QB>
+__global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ delta,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part, int B, int Hq,
+    int Hkv, int Sq, int S, int causal, int window, float scale, float scale_log2, int n_kt,
+    int n_pairs, int hs) {
+  typedef BF16 E;
+  constexpr int NW = 8;        // waves
+  constexpr int NP = 4;        // wave pairs, 32 keys each
+  constexpr int BC = 32 * NP;  // keys per workgroup
+  constexpr int BR = 32 * QB;  // query rows per streamed tile
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  typedef LdsTile<E, BR, D> QTile;
+  constexpr int kTileOps = dma_tile_ops<E, BR, D, NW>();
+  constexpr int kRowOff = 2 * QTile::kBytes;  // lse[64] then delta[64] (fp32)
+  constexpr int kStage = kRowOff + 512;
+  constexpr int kPBlock = 2048;  // one 32 x 32 bf16 P block, 32 bytes per lane
+  __shared__ __attribute__((aligned(1024))) char st0[kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[kStage];
+  __shared__ __attribute__((aligned(1024))) char st2[kStage];
+  __shared__ __attribute__((aligned(1024))) char pbuf[NP * QB * kPBlock];
+
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+  const bool srole = w < NP;  // S / P / dV wave (else dP / dS / dK)
+  const int pw = w & (NP - 1);
+  char* pslot = pbuf + pw * QB * kPBlock + lane * 16;
+
+  // Work item: (batch x KV head, head part, key-tile pair), dealt to XCDs in contiguous chunks.
+  const int T = B * Hkv * hs * n_pairs;
+  const int wi = (T % 8 == 0) ? (int)(blockIdx.x % 8) * (T / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int pair = wi % n_pairs;
+  const int t2 = wi / n_pairs;
+  const int hp = t2 % hs;
+  const int bg = t2 / hs;
+  const int b = bg / Hkv;
+  const int G = Hq / Hkv;
+  const int hpg = G / hs;
+  const int h0 = (bg - b * Hkv) * G + hp * hpg;
+  const int ta = pair;
+  const int tb = n_kt - 1 - pair;
+  const bool two = tb > ta;
+  const size_t kv_off = (size_t)bg * S * D;
+  const int qoff = S - Sq;  // query row r stands at key position r + qoff
+
+  int kt = ta, lo = 0, nq = 0, n_steps = 0;
+  auto set_segment = [&](int t) __attribute__((always_inline)) {
+    int hi;
+    kt = t;
+    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, &lo, &hi);
+    nq = imax_(hi - lo + 1, 0);  // 0: no query sees these keys, so dK = dV = 0
+    n_steps = hpg * nq;
+  };
+  // Query tiles run from the last one down, head by head; (hh, it) = head offset, tile counter.
+  auto issue = [&](int hh, int it, char* stg) __attribute__((always_inline)) {
+    const int i0 = (lo + nq - 1 - it) * BR;
+    const size_t bh = (size_t)b * Hq + h0 + hh;
+    dma_tile<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, Sq);
+    dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, Sq);
+    if (w == 0) dma_row_floats(stg + kRowOff, LSE2 + bh * Sq, i0, Sq);
+    if (w == 1) dma_row_floats(stg + kRowOff + 256, delta + bh * Sq, i0, Sq);
+  };
+  auto advance = [&](int& hh, int& it) __attribute__((always_inline)) {
+    if (++it == nq) {
+      it = 0;
+      ++hh;
+    }
+  };
+
+  Frag<E> kvf[DS];   // K (S role) or V (dP role) rows of this pair's keys: the B operand
+  f32x16_t acc[DB];  // dV (S role) or dK (dP role); register r holds key kw + acc_row(r)
+  auto load_kv = [&]() __attribute__((always_inline)) {
+    const int my_k = kt * BC + 32 * pw + l32;
+    const bool ok = my_k < S;
+    const uint16_t* src = (srole ? K : V) + kv_off + (size_t)my_k * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) kvf[s] = load_frag_global(src + 16 * s, ok);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+  };
+  auto flush = [&]() __attribute__((always_inline)) {
+    const int kw = kt * BC + 32 * pw;
+    const size_t nkv = (size_t)B * Hkv * S * D;
+    const float mul = srole ? 1.f : scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kw + acc_row(r);
+        if (key >= S) continue;
+        const size_t o = kv_off + (size_t)key * D + 32 * db + l32;
+        if (hs > 1) {
+          part[(size_t)(2 * hp + (srole ? 1 : 0)) * nkv + o] = acc[db][r];
+        } else {
+          (srole ? dV : dK)[o] = (uint16_t)bf16_bits(acc[db][r] * mul);
+        }
+      }
+    }
+  };
+
+  auto compute = [&](int it, const char* q_lds) __attribute__((always_inline)) {
+    const char* do_lds = q_lds + QTile::kBytes;
+    const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
+    const float* dl_lds = lse_lds + 64;
+    const int i0 = (lo + nq - 1 - it) * BR;
+    const int p0 = i0 + qoff;  // position of the tile's first row
+    const int kw = kt * BC + 32 * pw;
+    const int my_k = kw + l32;
+    f32x16_t xs[QB];  // S -> P (S role) or dP -> dS (dP role)
+    bool act[QB];
+    // Phase 1: S = Q K^T and P (S role), dP = dO V^T (dP role).
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int r0 = p0 + 32 * qb;
+      act[qb] = !block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window);
+      if (!act[qb]) continue;
+      const char* src = srole ? q_lds : do_lds;
+      Frag<E> fr[DS];
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) fr[s2] = RowFrag<E, QTile>::get(src, 32 * qb + l32, s2);
+      __builtin_amdgcn_sched_barrier(0);
+      xs[qb] = f32x16_t{};
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) mma(xs[qb], fr[s2], kvf[s2]);
+      if (srole) {
+        const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window);
+        auto softmax = [&](auto maskc) __attribute__((always_inline)) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int rb = 32 * qb + 8 * r4 + 4 * half;  // registers 4*r4 .. 4*r4+3: rows rb .. rb+3
+            const f32x4_t lse4 = *reinterpret_cast<const f32x4_t*>(lse_lds + rb);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int r = 4 * r4 + c;
+              float p = __builtin_amdgcn_exp2f(fmaf(xs[qb][r], scale_log2, -lse4[c]));
+              if constexpr (decltype(maskc)::value) {
+                if (!visible(p0 + rb + c, my_k, S, causal, window)) p = 0.f;
+              }
+              xs[qb][r] = p;
+            }
+          }
+        };
+        if (full) softmax(IC<0>{});
+        else softmax(IC<1>{});
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<u32x4_t*>(pslot + qb * kPBlock + t * 1024) = acc_frag<E>(xs[qb], t).v;
+      }
+    }
+    barrier_keep_vm();  // the P blocks are in LDS
+    // Phase 2: dV += P^T dO (S role); dS = P o (dP - delta), dK += dS^T Q (dP role).
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (!act[qb]) continue;
+      const char* tsrc = srole ? do_lds : q_lds;
+      if (!srole) {
+        const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pslot + qb * kPBlock);
+        const u32x4_t pb = *reinterpret_cast<const u32x4_t*>(pslot + qb * kPBlock + 1024);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int rb = 32 * qb + 8 * r4 + 4 * half;
+          const f32x4_t dl4 = *reinterpret_cast<const f32x4_t*>(dl_lds + rb);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * r4 + c;
+            const uint32_t word = (r < 8 ? pa : pb)[(r & 7) >> 1];
+            const float p = __uint_as_float((r & 1) ? (word & 0xFFFF0000u) : (word << 16));
+            xs[qb][r] = p * (xs[qb][r] - dl4[c]);
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        Frag<E> tr[DB];  // dO^T (S role) or Q^T (dP role), rows 32*qb + 16t ..
+#pragma unroll
+        for (int db = 0; db < DB; ++db) tr[db] = TrFrag<E, QTile>::get(tsrc, 32 * qb + 16 * t, 32 * db);
+        const Frag<E> af = acc_frag<E>(xs[qb], t);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) mma(acc[db], af, tr[db]);
+      }
+    }
+  };
+
+  int ch, ct, ih, iq;
+  auto step = [&](auto stc, int s) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stc)::value;
+    char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
+    char* nn = ST == 0 ? st2 : (ST == 1 ? st0 : st1);
+    if (s + 1 < n_steps) {
+      if (w < 2) wait_vmcnt<2 * kTileOps + 1>();
+      else wait_vmcnt<2 * kTileOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_keep_vm();
+    if (s + 2 < n_steps) {
+      issue(ih, iq, nn);
+      advance(ih, iq);
+    }
+    compute(ct, cur);
+    advance(ch, ct);
+  };
+  const int n_seg = two ? 2 : 1;
+  for (int seg = 0; seg < n_seg; ++seg) {
+    if (seg) barrier_keep_vm();  // every wave is done with the previous segment's stages
+    set_segment(seg ? tb : ta);
+    load_kv();
+    ch = 0, ct = 0, ih = 0, iq = 0;
+    if (n_steps > 0) {
+      issue(ih, iq, st0);
+      advance(ih, iq);
+    }
+    if (n_steps > 1) {
+      issue(ih, iq, st1);
+      advance(ih, iq);
+    }
+    wait_vmcnt<0>();
+    for (int s = 0; s < n_steps; s += 3) {
+      step(IC<0>{}, s);
+      if (s + 1 < n_steps) step(IC<1>{}, s + 1);
+      if (s + 2 < n_steps) step(IC<2>{}, s + 2);
+    }
+    flush();
+  }
+}
+
 template <class E>
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
                                                           typename E::T* __restrict__ dK,
@@ -286,12 +528,19 @@ static int launch_dkdv_t(const Args& a) {
     constexpr int NW = kDkdvWaves;
     constexpr int QB = E::kBytes == 2 ? 2 : 1;
     const DkdvPlan p = dkdv_plan(a.B, a.Hq, a.Hkv, a.Sk);
-    dim3 grid((unsigned)(p.n_pairs * a.B * a.Hkv * p.hs)), block(NW * 64);
+    dim3 grid((unsigned)(p.n_pairs * a.B * a.Hkv * p.hs));
     notify_launch("attn_bwd_dkdv", 0, a.stream);
-    hipLaunchKernelGGL((dkdv_kernel<E, D, NW, QB>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
-                       (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window,
-                       a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
+    if constexpr (E::kBytes == 2) {
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, QB>), grid, dim3(512), 0, st, (const T*)a.q,
+                         (const T*)a.k, (const T*)a.v, (const T*)a.dout, (const float*)a.lse2,
+                         (const float*)a.delta, (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq,
+                         a.Sk, a.causal, a.window, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<E, D, NW, QB>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
+                         (const T*)a.k, (const T*)a.v, (const T*)a.dout, (const float*)a.lse2,
+                         (const float*)a.delta, (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq,
+                         a.Sk, a.causal, a.window, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
+    }
     notify_launch("attn_bwd_dkdv", 1, a.stream);
     if (p.hs > 1) {
       const size_t n = (size_t)a.B * a.Hkv * a.Sk * D;
