@@ -22,6 +22,8 @@ What it computes is plain materialised softmax attention and its exact gradient,
   * "CUDA-LLM: A GitHub Repository for Development", section "The custom CUDA kernel": the kernel is
     generalised to fewer queries than keys (S_q <= S_k), so that one kernel serves a full prefill and
     a single-token decode against a cache.
+  * "KYNETRA FOUNDRY" page, Vaultecho paragraph: besides the sliding window of recent tokens a few
+    persistent "sink" tokens at the start of the sequence stay attended.
 
 Readings where the pages leave a step open (each also listed in the design notes):
   * tensors are [B, H, S, D] contiguous, D fastest; K and V have Hkv heads, Q/O/dO have Hq heads;
@@ -34,6 +36,9 @@ Readings where the pages leave a step open (each also listed in the design notes
   * with S_q <= S_k the queries are the last S_q positions: query i sits at absolute position
     i + (S_k - S_q) for the causal mask and the window ("bottom-right" alignment; a single decode query
     sees every key); S_q > S_k is not defined by the pages and is rejected;
+  * sinks: the first n_sink keys stay visible to every query at or after them even when the window
+    has moved past them (key j visible iff causal allows it and (p - j < W or j < n_sink)); without a
+    window every earlier key is visible anyway, so n_sink only matters when W > 0;
   * every row has at least one visible key (its own position), so no empty-row convention is needed.
 
 Rows are processed in blocks of `row_block` queries only to bound memory: each row's softmax is
@@ -52,8 +57,10 @@ __all__ = [
 ]
 
 
-def _check(q, k, v, causal, window):
+def _check(q, k, v, causal, window, sink=0):
     """Returns (B, Hq, Hkv, S_q, S_k, D)."""
+    if sink < 0:
+        raise ValueError("n_sink must be >= 0")
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be [B, H, S, D]")
     B, Hq, Sq, D = q.shape
@@ -77,25 +84,26 @@ def kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def visible_mask(rows, cols, causal: bool, window: int, offset: int = 0) -> np.ndarray:
+def visible_mask(rows, cols, causal: bool, window: int, offset: int = 0, sink: int = 0) -> np.ndarray:
     """Boolean [len(rows), len(cols)]: with query i at position p = i + offset, key j is visible
-    iff (not causal or j <= p) and (window == 0 or p - j < window). offset = S_k - S_q."""
+    iff (not causal or j <= p) and (window == 0 or p - j < window or j < sink).
+    offset = S_k - S_q; sink = number of sink keys."""
     i = np.asarray(rows, dtype=np.int64)[:, None] + offset
     j = np.asarray(cols, dtype=np.int64)[None, :]
     m = np.ones((i.shape[0], j.shape[1]), dtype=bool)
     if causal:
         m &= j <= i
     if window > 0:
-        m &= (i - j) < window
+        m &= ((i - j) < window) | (j < sink)
     return m
 
 
-def visible_count(i: int, S: int, causal: bool, window: int, offset: int = 0) -> int:
+def visible_count(i: int, S: int, causal: bool, window: int, offset: int = 0, sink: int = 0) -> int:
     """Number of the S keys visible to query i (counted from the mask definition)."""
-    return int(visible_mask([i], np.arange(S), causal, window, offset).sum())
+    return int(visible_mask([i], np.arange(S), causal, window, offset, sink).sum())
 
 
-def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0):
+def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0, sink=0):
     """One head, a set of query rows, all S_k keys.
 
     qh [S_q, D], kh/vh [S_k, D], doh [S_q, D] or None (float64); query i at position i + offset.
@@ -103,7 +111,7 @@ def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0):
     LSE [R], and when doh is given dP [R, S_k], delta [R] and dS [R, S_k]."""
     S = kh.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
-    mask = visible_mask(rows, np.arange(S), causal, window, offset)
+    mask = visible_mask(rows, np.arange(S), causal, window, offset, sink)
     x = scale * (qh[rows] @ kh.T)                     # scaled scores
     x = np.where(mask, x, -np.inf)
     m = x.max(axis=1, keepdims=True)                  # finite: the row's own position is visible
@@ -124,11 +132,11 @@ def _f64(*xs):
     return tuple(np.asarray(x, dtype=np.float64) for x in xs)
 
 
-def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256):
+def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256, sink=0):
     """Full attention forward (O, LSE) and, when do is given, backward (dQ, dK, dV).
 
     q, do [B,Hq,S_q,D]; k, v [B,Hkv,S_k,D] with S_q <= S_k. Returns float64 arrays in a dict."""
-    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window)
+    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
     off = Sk - S
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     q, k, v = _f64(q, k, v)
@@ -147,7 +155,7 @@ def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_bl
             for r0 in range(0, S, row_block):
                 rows = np.arange(r0, min(S, r0 + row_block))
                 t = head_rows(q[b, h], k[b, g], v[b, g], rows, causal, window, scale,
-                              None if do is None else do[b, h], off)
+                              None if do is None else do[b, h], off, sink)
                 O[b, h, rows] = t["O"]
                 LSE[b, h, rows] = t["LSE"]
                 if do is not None:
@@ -158,56 +166,56 @@ def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_bl
     return res
 
 
-def forward(q, k, v, causal=True, window=0, scale=None, row_block=256):
+def forward(q, k, v, causal=True, window=0, scale=None, row_block=256, sink=0):
     """Returns (O, LSE) in float64."""
-    r = forward_backward(q, k, v, None, causal, window, scale, row_block)
+    r = forward_backward(q, k, v, None, causal, window, scale, row_block, sink)
     return r["O"], r["LSE"]
 
 
-def backward(q, k, v, do, causal=True, window=0, scale=None, row_block=256):
+def backward(q, k, v, do, causal=True, window=0, scale=None, row_block=256, sink=0):
     """Returns (dQ, dK, dV) in float64: the exact gradient of sum(O * dO)."""
-    r = forward_backward(q, k, v, do, causal, window, scale, row_block)
+    r = forward_backward(q, k, v, do, causal, window, scale, row_block, sink)
     return r["dQ"], r["dK"], r["dV"]
 
 
-def probabilities(q, k, b, h, causal=True, window=0, scale=None):
+def probabilities(q, k, b, h, causal=True, window=0, scale=None, sink=0):
     """Softmax probabilities P [S_q, S_k] of one (batch, query head)."""
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     qh, kh = _f64(q[b, h], k[b, kv_head(h, Hq, Hkv)])
-    return head_rows(qh, kh, kh, np.arange(S), causal, window, scale, None, k.shape[2] - S)["P"]
+    return head_rows(qh, kh, kh, np.arange(S), causal, window, scale, None, k.shape[2] - S, sink)["P"]
 
 
-def rows_forward(q, k, v, b, h, rows, causal=True, window=0, scale=None):
+def rows_forward(q, k, v, b, h, rows, causal=True, window=0, scale=None, sink=0):
     """O[b, h, rows] and LSE[b, h, rows], each row computed on its own."""
-    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window)
+    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     g = kv_head(h, Hq, Hkv)
     qh, kh, vh = _f64(q[b, h], k[b, g], v[b, g])
-    t = head_rows(qh, kh, vh, rows, causal, window, scale, None, Sk - S)
+    t = head_rows(qh, kh, vh, rows, causal, window, scale, None, Sk - S, sink)
     return t["O"], t["LSE"]
 
 
-def rows_dq(q, k, v, do, b, h, rows, causal=True, window=0, scale=None):
+def rows_dq(q, k, v, do, b, h, rows, causal=True, window=0, scale=None, sink=0):
     """dQ[b, h, rows]: each row needs only its own probabilities and dP row."""
-    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window)
+    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     g = kv_head(h, Hq, Hkv)
     qh, kh, vh, doh = _f64(q[b, h], k[b, g], v[b, g], do[b, h])
-    t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S)
+    t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S, sink)
     return scale * (t["dS"] @ kh)
 
 
-def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_block=256):
+def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_block=256, sink=0):
     """dK[b, g, cols] and dV[b, g, cols]: sums over every query head of group g and every
     query row that can see at least one of `cols`."""
-    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window)
+    B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     cols = np.asarray(cols, dtype=np.int64)
     G = Hq // Hkv
     kh, vh = _f64(k[b, g], v[b, g])
-    need = visible_mask(np.arange(S), cols, causal, window, Sk - S).any(axis=1)
+    need = visible_mask(np.arange(S), cols, causal, window, Sk - S, sink).any(axis=1)
     rows_all = np.nonzero(need)[0]
     dK = np.zeros((cols.size, D))
     dV = np.zeros((cols.size, D))
@@ -215,7 +223,7 @@ def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_bl
         qh, doh = _f64(q[b, h], do[b, h])
         for r0 in range(0, rows_all.size, row_block):
             rows = rows_all[r0:r0 + row_block]
-            t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S)
+            t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S, sink)
             dK += scale * (t["dS"][:, cols].T @ qh[rows])
             dV += t["P"][:, cols].T @ doh[rows]
     return dK, dV

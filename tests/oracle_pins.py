@@ -13,7 +13,10 @@ a transposed operand, an off-by-one mask -- fails at least one of them):
     a row's visible set cannot change that row;
   * fewer queries than keys (S_q < S_k): a chunk of queries equals the last S_q rows of the square
     problem over all S_k positions (gradients with dO zero on the other rows), torch's own
-    lower-right causal bias, and a single decode query that sees every key (or the last W).
+    lower-right causal bias, and a single decode query that sees every key (or the last W);
+  * sink keys with a window: a decode query equals plain attention over the sink keys and the last
+    W keys cut out and concatenated; sinks covering every key give plain causal attention; zero-query
+    counts are the size of the union of the window and the sink range.
 """
 from __future__ import annotations
 
@@ -102,7 +105,7 @@ def pin_fd_sampled(A, seed=1, n_entries=256, n_dirs=16, tol=1e-6):
 
 
 # ---------------------------------------------------------------- scalar brute force
-def _brute(q, k, v, do, causal, window, scale):
+def _brute(q, k, v, do, causal, window, scale, sink=0):
     """Pure-Python loops; softmax derivative through the full Jacobian dP_k/dx_j = P_k (d_kj - P_j).
     With Sq queries and Sk keys, query i stands at position i + Sk - Sq."""
     B, Hq, S, D = q.shape
@@ -119,7 +122,7 @@ def _brute(q, k, v, do, causal, window, scale):
             for i in range(S):
                 pos = i + Sk - S
                 vis = [j for j in range(Sk)
-                       if (not causal or j <= pos) and (window == 0 or pos - j < window)]
+                       if (not causal or j <= pos) and (window == 0 or pos - j < window or j < sink)]
                 x = {j: scale * sum(q[b, h, i, d] * k[b, g, j, d] for d in range(D)) for j in vis}
                 mx = max(x.values())
                 z = sum(math.exp(x[j] - mx) for j in vis)
@@ -139,21 +142,23 @@ def _brute(q, k, v, do, causal, window, scale):
 
 
 def pin_bruteforce(A, tol=1e-12):
-    for (B, Hq, Hkv, S, Sk, D, causal, window, seed) in (
-        (1, 2, 2, 7, 7, 3, True, 0, 3), (2, 4, 2, 9, 9, 4, True, 3, 4), (1, 3, 1, 6, 6, 2, False, 0, 5),
-        (1, 4, 4, 8, 8, 5, True, 1, 6), (1, 2, 1, 5, 5, 3, True, 9, 7),
-        (1, 2, 1, 3, 8, 3, True, 0, 8), (2, 4, 2, 4, 9, 2, True, 3, 9), (1, 2, 2, 1, 6, 3, True, 0, 10),
-        (1, 2, 1, 1, 7, 2, True, 2, 14), (1, 3, 3, 4, 6, 2, False, 0, 15),
+    for (B, Hq, Hkv, S, Sk, D, causal, window, seed, sink) in (
+        (1, 2, 2, 7, 7, 3, True, 0, 3, 0), (2, 4, 2, 9, 9, 4, True, 3, 4, 0), (1, 3, 1, 6, 6, 2, False, 0, 5, 0),
+        (1, 4, 4, 8, 8, 5, True, 1, 6, 0), (1, 2, 1, 5, 5, 3, True, 9, 7, 0),
+        (1, 2, 1, 3, 8, 3, True, 0, 8, 0), (2, 4, 2, 4, 9, 2, True, 3, 9, 0), (1, 2, 2, 1, 6, 3, True, 0, 10, 0),
+        (1, 2, 1, 1, 7, 2, True, 2, 14, 0), (1, 3, 3, 4, 6, 2, False, 0, 15, 0),
+        (1, 2, 1, 9, 9, 3, True, 2, 16, 2), (2, 2, 2, 5, 10, 2, True, 3, 17, 1), (1, 4, 2, 10, 10, 2, True, 1, 18, 3),
+        (1, 2, 1, 1, 9, 3, True, 2, 19, 3),
     ):
         q, k, v, do = _rng_inputs(seed, B, Hq, Hkv, S, D, Sk=Sk)
         scale = 0.7
-        r = A.forward_backward(q, k, v, do, causal, window, scale)
-        ref = _brute(q, k, v, do, causal, window, scale)
+        r = A.forward_backward(q, k, v, do, causal, window, scale, sink=sink)
+        ref = _brute(q, k, v, do, causal, window, scale, sink)
         for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"),
                               (r["O"], r["LSE"], r["dQ"], r["dK"], r["dV"]), ref):
             err = np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30)
-            assert err <= tol, (f"brute force {name} (S={S}, Sk={Sk}, W={window}, causal={causal}): "
-                                f"{err:.3e}")
+            assert err <= tol, (f"brute force {name} (S={S}, Sk={Sk}, W={window}, causal={causal}, "
+                                f"sink={sink}): {err:.3e}")
 
 
 # ---------------------------------------------------------------- library routine
@@ -438,10 +443,96 @@ def pin_chunk_helpers(A):
         assert np.max(np.abs(dv - r["dV"][0, 1, cols])) <= 1e-13
 
 
+# ---------------------------------------------------------------- sink keys with a window
+def pin_sink_decode_is_concatenation(A):
+    """One decode query at the last position with a window W and n sink keys sees exactly keys
+    0..n-1 and S_k-W..S_k-1: plain (unmasked) attention over those rows cut out of K and V and
+    concatenated gives the same O, LSE, dQ, and dK / dV scattered back (zero elsewhere)."""
+    Sk, D = 40, 8
+    q, k, v, do = _rng_inputs(36, 1, 4, 2, 1, D, Sk=Sk)
+    for n, W in ((1, 5), (3, 7), (4, 1), (6, 34)):
+        idx = np.r_[np.arange(n), np.arange(Sk - W, Sk)]
+        r = A.forward_backward(q, k, v, do, True, W, 0.6, sink=n)
+        sub = A.forward_backward(q, k[:, :, idx], v[:, :, idx], do, False, 0, 0.6)
+        for name in ("O", "LSE", "dQ"):
+            assert np.max(np.abs(r[name] - sub[name])) <= 1e-14, f"sink decode n={n} W={W} {name}"
+        for name in ("dK", "dV"):
+            full = np.zeros_like(r[name])
+            full[:, :, idx] = sub[name]
+            assert np.max(np.abs(r[name] - full)) <= 1e-14, f"sink decode n={n} W={W} {name}"
+
+
+def pin_sinks_covering_all_keys(A):
+    """With at least as many sink keys as keys, the window no longer hides anything: the result is
+    plain causal attention; with no sink keys it is the window alone."""
+    q, k, v, do = _rng_inputs(37, 1, 4, 2, 30, 8)
+    full = A.forward_backward(q, k, v, do, True, 0, 0.5)
+    for W in (1, 4, 17):
+        r = A.forward_backward(q, k, v, do, True, W, 0.5, sink=30)
+        for name in ("O", "LSE", "dQ", "dK", "dV"):
+            assert np.max(np.abs(r[name] - full[name])) <= 1e-14, f"sink=S W={W} {name}"
+        r0 = A.forward_backward(q, k, v, do, True, W, 0.5, sink=0)
+        w0 = A.forward_backward(q, k, v, do, True, W, 0.5)
+        for name in ("O", "LSE", "dQ", "dK", "dV"):
+            assert np.array_equal(r0[name], w0[name]), f"sink=0 W={W} {name}"
+
+
+def pin_sink_zero_query_counts(A):
+    """Q = 0: exp(LSE) is the number of visible keys, the size of the union of the window
+    [p-W+1, p] and the sink keys [0, n-1] (those at or before p)."""
+    D = 4
+    for S, Sk in ((90, 90), (25, 90)):
+        q, k, v, do = _rng_inputs(38, 1, 2, 1, S, D, Sk=Sk)
+        q[:] = 0.0
+        for W, n in ((1, 1), (8, 3), (8, 8), (8, 20), (33, 64), (64, 1)):
+            _, LSE = A.forward(q, k, v, True, W, 1.0, sink=n)
+            p = np.arange(S) + Sk - S
+            lo = np.maximum(0, p - W + 1)                       # first key of the window
+            extra = np.clip(np.minimum(n, p + 1) - 0, 0, None)  # sink keys at or before p ...
+            extra = np.maximum(0, np.minimum(extra, lo))        # ... that lie before the window
+            want = (p - lo + 1) + extra
+            got = np.rint(np.exp(LSE[0, 0])).astype(np.int64)
+            assert np.array_equal(got, want), (S, Sk, W, n)
+
+
+def pin_sink_chunk_is_suffix_of_square(A):
+    """Sinks with fewer queries than keys: still the last rows of the square problem."""
+    Sk, D = 33, 8
+    qf, k, v, dof = _rng_inputs(39, 1, 2, 2, Sk, D)
+    for S, W, n in ((11, 4, 2), (1, 6, 3), (20, 9, 5)):
+        q, do = qf[:, :, Sk - S:], dof[:, :, Sk - S:]
+        r = A.forward_backward(q, k, v, do, True, W, 0.45, sink=n)
+        dz = dof.copy()
+        dz[:, :, :Sk - S] = 0.0
+        full = A.forward_backward(qf, k, v, dz, True, W, 0.45, sink=n)
+        for name in ("O", "LSE", "dQ"):
+            assert np.max(np.abs(r[name] - full[name][:, :, Sk - S:])) <= 1e-13, (S, W, n, name)
+        for name in ("dK", "dV"):
+            assert np.max(np.abs(r[name] - full[name])) <= 1e-13, (S, W, n, name)
+
+
+def pin_sink_helpers(A):
+    """Row / column helpers agree with the full pass with sinks."""
+    q, k, v, do = _rng_inputs(40, 1, 4, 2, 30, 8, Sk=45)
+    r = A.forward_backward(q, k, v, do, True, 7, 0.4, row_block=8, sink=3)
+    rows = np.array([0, 13, 29])
+    O, LSE = A.rows_forward(q, k, v, 0, 1, rows, True, 7, 0.4, sink=3)
+    assert np.max(np.abs(O - r["O"][0, 1, rows])) <= 1e-14
+    assert np.max(np.abs(LSE - r["LSE"][0, 1, rows])) <= 1e-14
+    dq = A.rows_dq(q, k, v, do, 0, 1, rows, True, 7, 0.4, sink=3)
+    assert np.max(np.abs(dq - r["dQ"][0, 1, rows])) <= 1e-13
+    cols = np.array([0, 2, 3, 20, 44])
+    dk, dv = A.cols_dkdv(q, k, v, do, 0, 0, cols, True, 7, 0.4, row_block=5, sink=3)
+    assert np.max(np.abs(dk - r["dK"][0, 0, cols])) <= 1e-13
+    assert np.max(np.abs(dv - r["dV"][0, 0, cols])) <= 1e-13
+
+
 ALL_PINS = [
     pin_fd_every_entry, pin_bruteforce, pin_torch_sdpa, pin_three_token_closed_form,
     pin_constant_v, pin_identical_keys, pin_window_one, pin_zero_queries, pin_rows_sum_to_one,
     pin_gradient_identities, pin_gqa_is_repeated_mha, pin_hidden_keys_do_not_matter,
     pin_row_and_column_helpers, pin_chunk_is_suffix_of_square, pin_torch_lower_right_causal,
-    pin_single_decode_query, pin_chunk_helpers,
+    pin_single_decode_query, pin_chunk_helpers, pin_sink_decode_is_concatenation,
+    pin_sinks_covering_all_keys, pin_sink_zero_query_counts, pin_sink_chunk_is_suffix_of_square,
+    pin_sink_helpers,
 ]

@@ -14,8 +14,8 @@ _real_mask = A.visible_mask
 
 
 def _head_rows_mut(kind):
-    def f(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0):
-        t = _real_head_rows(qh, kh, vh, rows, causal, window, scale, doh, offset)
+    def f(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0, sink=0):
+        t = _real_head_rows(qh, kh, vh, rows, causal, window, scale, doh, offset, sink)
         if doh is not None:
             if kind == "dropped_delta":          # dS = P * dP (rowsum term dropped)
                 t["dS"] = t["P"] * t["dP"]
@@ -32,8 +32,8 @@ def _head_rows_mut(kind):
 
 
 def _fb_mut(kind):
-    def f(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256):
-        r = _real_fb(q, k, v, do, causal, window, scale, row_block)
+    def f(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256, sink=0):
+        r = _real_fb(q, k, v, do, causal, window, scale, row_block, sink)
         s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
         if kind == "lse_base2":
             r["LSE"] = r["LSE"] / math.log(2.0)
@@ -47,7 +47,7 @@ def _fb_mut(kind):
 
 
 def _mask_mut(kind):
-    def f(rows, cols, causal, window, offset=0):
+    def f(rows, cols, causal, window, offset=0, sink=0):
         if kind == "offset_ignored":          # queries aligned top-left instead of bottom-right
             offset = 0
         elif kind == "offset_negated":
@@ -58,7 +58,17 @@ def _mask_mut(kind):
         if causal:
             m &= (j < i) | (j == i) if kind != "causal_transposed" else (j >= i)
         if window > 0:
-            m &= ((i - j) <= window) if kind == "window_off_by_one" else ((i - j) < window)
+            inw = ((i - j) <= window) if kind == "window_off_by_one" else ((i - j) < window)
+            if kind == "sink_ignored":
+                sk = inw
+            elif kind == "sink_off_by_one":       # one sink key too many
+                sk = inw | (j <= sink)
+            elif kind == "sink_without_causal":   # sinks visible even to earlier queries
+                sk = inw | (j < sink)
+                m = (m | (j < sink)) if causal else m
+            else:
+                sk = inw | (j < sink)
+            m &= sk
         return m
     return f
 
@@ -76,6 +86,9 @@ MUTANTS = {
     "causal_transposed": ("visible_mask", _mask_mut("causal_transposed")),
     "offset_ignored": ("visible_mask", _mask_mut("offset_ignored")),
     "offset_negated": ("visible_mask", _mask_mut("offset_negated")),
+    "sink_ignored": ("visible_mask", _mask_mut("sink_ignored")),
+    "sink_off_by_one": ("visible_mask", _mask_mut("sink_off_by_one")),
+    "sink_without_causal": ("visible_mask", _mask_mut("sink_without_causal")),
 }
 
 # Pins that run quickly enough to try on every mutant.
