@@ -9,7 +9,7 @@ FLOPs are counted as 4*B*Hq*N*D for the forward, with N = S^2/2 attended pairs u
 mask (the exact pair count with a window, S^2 without a mask), and 2.5x that for the backward.
 With fewer queries than keys (--workload naming a prefill-chunk or decode shape: Sq queries at
 the last Sq of S positions) N = (S^2 - (S-Sq)^2)/2 causal, the exact count with a window, Sq*S
-without a mask.
+without a mask; sink keys add the exact count of sink keys outside each row's window.
 """
 from __future__ import annotations
 
@@ -38,8 +38,9 @@ KERNEL_SOURCES = {
 }
 
 
-def attended_pairs(S: int, causal: bool, window: int, Sq: int | None = None) -> float:
-    """Attended (query, key) pairs for Sq queries at the last Sq of S key positions."""
+def attended_pairs(S: int, causal: bool, window: int, Sq: int | None = None, sink: int = 0) -> float:
+    """Attended (query, key) pairs for Sq queries at the last Sq of S key positions, with `sink`
+    leading keys kept visible beside the window."""
     Sq = S if Sq is None else Sq
     off = S - Sq
     if not causal:
@@ -50,7 +51,14 @@ def attended_pairs(S: int, causal: bool, window: int, Sq: int | None = None) -> 
     def upto(n):  # sum over positions p < n of min(p + 1, W)
         W = min(window, n)
         return W * (W + 1) / 2.0 + (n - W) * window
-    return upto(S) - upto(off)
+
+    def sinks_upto(n):  # sum over positions p < n of the sink keys before the window: min(n_sink, p-W+1)+
+        total = 0.0
+        for p in range(window, n):  # only positions whose window starts after key 0
+            total += min(sink, p - window + 1)
+        return total
+    extra = sinks_upto(S) - sinks_upto(off) if sink else 0.0
+    return upto(S) - upto(off) + extra
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -130,9 +138,9 @@ def cpu_baseline(w, q, k, v, do, heads: int):
     groups = heads // G
     t0 = time.perf_counter()
     oracle.forward_backward(q[:, :heads], k[:, :groups], v[:, :groups], do[:, :heads],
-                            w.causal, w.window, w.scale)
+                            w.causal, w.window, w.scale, sink=w.sink)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.B * heads * attended_pairs(w.S, w.causal, w.window, w.n_q) * w.D * 3.5
+    flops = 4.0 * w.B * heads * attended_pairs(w.S, w.causal, w.window, w.n_q, w.sink) * w.D * 3.5
     model, blas = host_info()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle fwd+bwd on {heads} of {w.Hq} query heads ({groups} KV groups), "
@@ -187,14 +195,20 @@ def main() -> int:
     ws_bytes = fa.attn_bwd_qk_workspace_bytes(w.B, w.Hq, w.Hkv, Sq, w.S, w.D)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     # the square workloads go through attn_fwd / attn_bwd, the others through the _qk entry points
-    fwd_call = fa.attn_fwd if Sq == w.S else fa.attn_fwd_qk
-    bwd_call = fa.attn_bwd if Sq == w.S else fa.attn_bwd_qk
+    square = Sq == w.S and not w.sink
 
     def fwd():
-        fwd_call(tq, tk, tv, o, lse, w.causal, w.window, w.scale)
+        if square:
+            fa.attn_fwd(tq, tk, tv, o, lse, w.causal, w.window, w.scale)
+        else:
+            fa.attn_fwd_qk(tq, tk, tv, o, lse, w.causal, w.window, w.scale, None, w.sink)
 
     def bwd():
-        bwd_call(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window, w.scale)
+        if square:
+            fa.attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window, w.scale)
+        else:
+            fa.attn_bwd_qk(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window, w.scale, None,
+                           w.sink)
 
     def step():
         fwd()
@@ -250,7 +264,7 @@ def main() -> int:
         d = [evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2)]
         kern_ms[name] = sum(d) / len(d)
 
-    N = attended_pairs(w.S, w.causal, w.window, Sq)
+    N = attended_pairs(w.S, w.causal, w.window, Sq, w.sink)
     unit = 2.0 * w.B * w.Hq * N * w.D  # one GEMM-sized pass over the attended pairs
     fl = {"attn_fwd": 2 * unit, "attn_bwd_dkdv": 4 * unit, "attn_bwd_dq": 1 * unit}
     total_flops = 7 * unit  # forward (2) + backward counted as 2.5x forward (5)
@@ -290,7 +304,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
                    "causal": w.causal, "window": w.window, "parallelism": "none (1 GPU)",
-                   **({"Sq": Sq} if Sq != w.S else {})},
+                   **({"Sq": Sq} if Sq != w.S else {}), **({"sink": w.sink} if w.sink else {})},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "phase_ms": phases,
         "phase_tflops_median": {

@@ -46,10 +46,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.attn_fwd_qk.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_qk.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp]
     lib.attn_fwd_qk.restype = i
     lib.attn_bwd_qk.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                                i, i, i, i, i, i, i, i, f, vp]
+                                i, i, i, i, i, i, i, i, i, f, vp]
     lib.attn_bwd_qk.restype = i
     lib.attn_bwd_qk_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
@@ -154,11 +154,12 @@ def attn_fwd(q, k, v, o, lse, causal: bool = True, window: int = 0, scale: float
 
 
 def attn_fwd_qk(q, k, v, o, lse, causal: bool = True, window: int = 0, scale: float | None = None,
-                stream=None) -> None:
+                stream=None, sink: int = 0) -> None:
     """Calls attn_fwd_qk: q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] with Sq <= Sk (the queries are the last
-    Sq positions) -> o [B,Hq,Sq,D], lse [B,Hq,Sq] f32."""
-    ptrs, (B, Hq, Hkv, Sq, Sk, D), tail = _fwd_args(q, k, v, o, lse, causal, window, scale)
-    st = load_library().attn_fwd_qk(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, Sk, D, *tail,
+    Sq positions), `sink` leading keys kept visible beside the window -> o [B,Hq,Sq,D],
+    lse [B,Hq,Sq] f32."""
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), (c, w, sc) = _fwd_args(q, k, v, o, lse, causal, window, scale)
+    st = load_library().attn_fwd_qk(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, Sk, D, c, w, int(sink), sc,
                                     _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_qk")
@@ -199,34 +200,37 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = True, 
 
 
 def attn_bwd_qk(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = True,
-                window: int = 0, scale: float | None = None, stream=None) -> None:
-    """Calls attn_bwd_qk (Sq <= Sk); dq/dk/dv are overwritten. workspace: a uint8 GPU tensor of
-    at least attn_bwd_qk_workspace_bytes(...) bytes."""
-    ptrs, (B, Hq, Hkv, Sq, Sk, D), tail = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace,
-                                                    causal, window, scale)
-    st = load_library().attn_bwd_qk(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, Sk, D, *tail,
+                window: int = 0, scale: float | None = None, stream=None, sink: int = 0) -> None:
+    """Calls attn_bwd_qk (Sq <= Sk, `sink` sink keys); dq/dk/dv are overwritten. workspace: a uint8
+    GPU tensor of at least attn_bwd_qk_workspace_bytes(...) bytes."""
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), (c, w, sc) = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv,
+                                                          workspace, causal, window, scale)
+    st = load_library().attn_bwd_qk(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, Sk, D, c, w, int(sink), sc,
                                     _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_qk")
 
 
 # ---------------------------------------------------------------- allocation conveniences
-def forward(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None, stream=None):
+def forward(q, k, v, causal: bool = True, window: int = 0, scale: float | None = None, stream=None,
+            sink: int = 0):
     """Allocates o and lse with torch, then calls attn_fwd (attn_fwd_qk when k has more rows than
-    q). Returns (o, lse)."""
+    q or there are sink keys). Returns (o, lse)."""
     import torch
     B, Hq, Sq, D = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    call = attn_fwd if k.shape[2] == Sq else attn_fwd_qk
-    call(q, k, v, o, lse, causal, window, scale, stream)
+    if k.shape[2] == Sq and not sink:
+        attn_fwd(q, k, v, o, lse, causal, window, scale, stream)
+    else:
+        attn_fwd_qk(q, k, v, o, lse, causal, window, scale, stream, sink)
     return o, lse
 
 
 def backward(q, k, v, o, lse, dout, causal: bool = True, window: int = 0,
-             scale: float | None = None, stream=None, workspace=None):
+             scale: float | None = None, stream=None, workspace=None, sink: int = 0):
     """Allocates dq, dk, dv (and the workspace if none is given), then calls attn_bwd
-    (attn_bwd_qk when k has more rows than q)."""
+    (attn_bwd_qk when k has more rows than q or there are sink keys)."""
     import torch
     B, Hq, Sq, D = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
@@ -236,6 +240,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, window: int = 0,
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    call = attn_bwd if Sk == Sq else attn_bwd_qk
-    call(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale, stream)
+    if Sk == Sq and not sink:
+        attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale, stream)
+    else:
+        attn_bwd_qk(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale, stream, sink)
     return dq, dk, dv

@@ -7,7 +7,8 @@
 // "CUDA-LLM: A GitHub Repository for Development", section "The custom CUDA kernel", only ever
 // narrows causal attention); with fewer queries than keys the queries are the last Sq positions
 // (same section: one kernel for prefill and for one-token decode against a cache), and more
-// queries than keys is not defined.
+// queries than keys is not defined; sink keys ("KYNETRA FOUNDRY", Vaultecho paragraph) are a count
+// >= 0 of leading keys that stay visible beside the window.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -22,10 +23,10 @@ attn_launch_hook_t g_hook = nullptr;
 void* g_hook_user = nullptr;
 
 int check_common(int dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
-                 int window, float scale) {
+                 int window, int sink, float scale) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || D <= 0) return ATTN_ERR_INVALID;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
-  if (window < 0) return ATTN_ERR_INVALID;
+  if (window < 0 || sink < 0) return ATTN_ERR_INVALID;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
@@ -55,10 +56,10 @@ void attn_set_launch_hook(attn_launch_hook_t hook, void* user) {
 
 
 int attn_fwd_qk(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, float scale,
-                void* stream) {
+                int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, int sink,
+                float scale, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
-  int st = check_common(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
+  int st = check_common(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, scale);
   if (st != ATTN_OK) return st;
   fa::Args a{};
   a.dtype = dtype;
@@ -75,6 +76,7 @@ int attn_fwd_qk(int dtype, const void* q, const void* k, const void* v, void* o,
   a.D = D;
   a.causal = causal;
   a.window = window;
+  a.sink = sink;
   a.scale = scale;
   a.stream = stream;
   return fa::launch_fwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
@@ -82,11 +84,11 @@ int attn_fwd_qk(int dtype, const void* q, const void* k, const void* v, void* o,
 
 int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B,
              int Hq, int Hkv, int S, int D, int causal, int window, float scale, void* stream) {
-  return attn_fwd_qk(dtype, q, k, v, o, lse, B, Hq, Hkv, S, S, D, causal, window, scale, stream);
+  return attn_fwd_qk(dtype, q, k, v, o, lse, B, Hq, Hkv, S, S, D, causal, window, 0, scale, stream);
 }
 
 size_t attn_bwd_qk_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
-  if (check_common(ATTN_BF16, B, Hq, Hkv, Sq, Sk, D, 1, 0, 1.0f) != ATTN_OK) return 0;
+  if (check_common(ATTN_BF16, B, Hq, Hkv, Sq, Sk, D, 1, 0, 0, 1.0f) != ATTN_OK) return 0;
   return fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D);
 }
 
@@ -97,10 +99,10 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
 int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const void* o,
                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                 size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
-                int window, float scale, void* stream) {
+                int window, int sink, float scale, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return ATTN_ERR_INVALID;
-  int st = check_common(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, scale);
+  int st = check_common(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, scale);
   if (st != ATTN_OK) return st;
   if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)) return ATTN_ERR_INVALID;
   fa::Args a{};
@@ -126,6 +128,7 @@ int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const vo
   a.D = D;
   a.causal = causal;
   a.window = window;
+  a.sink = sink;
   a.scale = scale;
   a.stream = stream;
   return fa::launch_bwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
@@ -136,7 +139,7 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
              size_t workspace_bytes, int B, int Hq, int Hkv, int S, int D, int causal, int window,
              float scale, void* stream) {
   return attn_bwd_qk(dtype, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq,
-                     Hkv, S, S, D, causal, window, scale, stream);
+                     Hkv, S, S, D, causal, window, 0, scale, stream);
 }
 
 const char* attn_status_string(int status) {

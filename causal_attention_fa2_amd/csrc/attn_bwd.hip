@@ -66,7 +66,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dQ,
-    int B, int Hq, int Hkv, int Sq, int S, int causal, int window, float scale, float scale_log2,
+    int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale,
+    float scale_log2,
     int n_qt) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 32 * KB;
@@ -106,11 +107,14 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   const int pw = qw + off;  // positions of this wave's rows
   const int my_p = my_q + off;
 
-  int jt_lo, jt_hi;
-  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, &jt_lo, &jt_hi);
-  const int n_steps = jt_hi - jt_lo + 1;
+  // key tiles: the sink tiles [0, jt_ns) then the window tiles [jt_lo, jt_hi]
+  int jt_ns, jt_lo, jt_hi;
+  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, sink, &jt_ns, &jt_lo,
+                &jt_hi);
+  const int n_steps = jt_ns + jt_hi - jt_lo + 1;
+  auto tile_of = [&](int s) __attribute__((always_inline)) { return s < jt_ns ? s : jt_lo + s - jt_ns; };
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
-    const int j0 = (jt_lo + s) * BC;
+    const int j0 = tile_of(s) * BC;
     dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
     dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
   };
@@ -133,9 +137,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
 
   auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
     const char* v_lds = k_lds + KvTile::kBytes;
-    const int j0 = (jt_lo + s) * BC;
-    if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window)) return;
-    const bool full = block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window);
+    const int j0 = tile_of(s) * BC;
+    if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink)) return;
+    const bool full = block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16_t st = f32x16_t{}, dpt = f32x16_t{};
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(fmaf(st[r], scale_log2, nlse2));
           if constexpr (decltype(maskc)::value) {
-            if (!visible(my_p, j0 + 32 * kb + acc_row(r), S, causal, window)) p = 0.f;
+            if (!visible(my_p, j0 + 32 * kb + acc_row(r), S, causal, window, sink)) p = 0.f;
           }
           st[r] = p * (dpt[r] - dl);
         }
@@ -222,7 +226,8 @@ static int launch_bwd_t(const Args& a) {
     notify_launch("attn_bwd_dq", 0, a.stream);
     hipLaunchKernelGGL((dq_kernel<E, D, NW, KB>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
-                       (T*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.scale, scale_log2,
+                       (T*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, a.scale,
+                       scale_log2,
                        n_qt);
     notify_launch("attn_bwd_dq", 1, a.stream);
   }

@@ -17,7 +17,8 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dK,
     typename E::T* __restrict__ dV, float* __restrict__ part, int B, int Hq, int Hkv, int Sq,
-    int S, int causal, int window, float scale, float scale_log2, int n_kt, int n_pairs, int hs) {
+    int S, int causal, int window, int sink, float scale, float scale_log2, int n_kt, int n_pairs,
+    int hs) {
   constexpr int BC = 32 * NW;  // keys per workgroup
   constexpr int BR = 32 * QB;  // query rows per streamed tile
   constexpr int DS = D / 16;
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   auto set_segment = [&](int t) __attribute__((always_inline)) {
     int hi;
     kt = t;
-    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, &lo, &hi);
+    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, sink, &lo, &hi);
     nq = imax_(hi - lo + 1, 0);  // 0: no query sees these keys, so dK = dV = 0
     n_steps = hpg * nq;
   };
@@ -134,8 +135,8 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int r0 = p0 + 32 * qb;
-      if (block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window)) continue;
-      const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window);
+      if (block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window, sink)) continue;
+      const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
       // All Q / dO row fragments of this block in flight before the S / dP products, so the
       // LDS latency is paid once per block rather than once per MFMA.
       Frag<E> qa[DS], da[DS];
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
             const int r = 4 * r4 + c;
             float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse4[c]));
             if constexpr (decltype(maskc)::value) {
-              if (!visible(p0 + rb + c, my_k, S, causal, window)) p = 0.f;
+              if (!visible(p0 + rb + c, my_k, S, causal, window, sink)) p = 0.f;
             }
             sa[r] = p;
             dp[r] = p * (dp[r] - dl4[c]);
@@ -271,7 +272,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part, int B, int Hq,
-    int Hkv, int Sq, int S, int causal, int window, float scale, float scale_log2, int n_kt,
+    int Hkv, int Sq, int S, int causal, int window, int sink, float scale, float scale_log2,
+    int n_kt,
     int n_pairs, int hs) {
   typedef BF16 E;
   constexpr int NW = 8;        // waves
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   auto set_segment = [&](int t) __attribute__((always_inline)) {
     int hi;
     kt = t;
-    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, &lo, &hi);
+    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, sink, &lo, &hi);
     nq = imax_(hi - lo + 1, 0);  // 0: no query sees these keys, so dK = dV = 0
     n_steps = hpg * nq;
   };
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int r0 = p0 + 32 * qb;
-      act[qb] = !block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window);
+      act[qb] = !block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
       if (!act[qb]) continue;
       const char* src = srole ? q_lds : do_lds;
       Frag<E> fr[DS];
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
 #pragma unroll
       for (int s2 = 0; s2 < DS; ++s2) mma(xs[qb], fr[s2], kvf[s2]);
       if (srole) {
-        const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window);
+        const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
         auto softmax = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
               const int r = 4 * r4 + c;
               float p = __builtin_amdgcn_exp2f(fmaf(xs[qb][r], scale_log2, -lse4[c]));
               if constexpr (decltype(maskc)::value) {
-                if (!visible(p0 + rb + c, my_k, S, causal, window)) p = 0.f;
+                if (!visible(p0 + rb + c, my_k, S, causal, window, sink)) p = 0.f;
               }
               xs[qb][r] = p;
             }
@@ -534,12 +536,12 @@ static int launch_dkdv_t(const Args& a) {
       hipLaunchKernelGGL((dkdv_pair_kernel<D, QB>), grid, dim3(512), 0, st, (const T*)a.q,
                          (const T*)a.k, (const T*)a.v, (const T*)a.dout, (const float*)a.lse2,
                          (const float*)a.delta, (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq,
-                         a.Sk, a.causal, a.window, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
+                         a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
     } else {
       hipLaunchKernelGGL((dkdv_kernel<E, D, NW, QB>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
                          (const T*)a.k, (const T*)a.v, (const T*)a.dout, (const float*)a.lse2,
                          (const float*)a.delta, (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq,
-                         a.Sk, a.causal, a.window, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
+                         a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
     }
     notify_launch("attn_bwd_dkdv", 1, a.stream);
     if (p.hs > 1) {

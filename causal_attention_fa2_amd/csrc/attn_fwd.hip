@@ -30,7 +30,8 @@ template <class E, int D, int NW, int KB, int NST>
 __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
-    int B, int Hq, int Hkv, int Sq, int S, int causal, int window, float scale_log2, int n_qt) {
+    int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale_log2,
+    int n_qt) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 32 * KB;
   constexpr int DS = D / 16;  // 16-wide contraction steps over the head dimension
@@ -69,12 +70,15 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   const int pw = qw + off;     // positions of this wave's rows: pw .. pw + 31
   const int my_p = my_q + off;
 
-  int jt_lo, jt_hi;
-  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, &jt_lo, &jt_hi);
-  const int n_steps = jt_hi - jt_lo + 1;
+  // key tiles: the sink tiles [0, jt_ns) then the window tiles [jt_lo, jt_hi]
+  int jt_ns, jt_lo, jt_hi;
+  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, sink, &jt_ns, &jt_lo,
+                &jt_hi);
+  const int n_steps = jt_ns + jt_hi - jt_lo + 1;
+  auto tile_of = [&](int s) __attribute__((always_inline)) { return s < jt_ns ? s : jt_lo + s - jt_ns; };
 
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
-    const int j0 = (jt_lo + s) * BC;
+    const int j0 = tile_of(s) * BC;
     dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
     dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
   };
@@ -126,7 +130,8 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (!visible(my_p, j0 + 32 * kb + acc_row(r), S, causal, window)) st[kb][r] = kNegInf;
+          if (!visible(my_p, j0 + 32 * kb + acc_row(r), S, causal, window, sink))
+            st[kb][r] = kNegInf;
           mx = fmaxf(mx, st[kb][r]);
         }
       }
@@ -178,9 +183,9 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   };
 
   auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
-    const int j0 = (jt_lo + s) * BC;
-    if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window)) return;
-    compute_general(j0, k_lds, block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window));
+    const int j0 = tile_of(s) * BC;
+    if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink)) return;
+    compute_general(j0, k_lds, block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink));
   };
 
   ring_run<NST, kStage, kOps>(ring, n_steps, issue, compute);
@@ -216,6 +221,7 @@ static int launch_fwd_t(const Args& a) {
   hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NST>), grid, block, 0, (hipStream_t)a.stream,
                      (const typename E::T*)a.q, (const typename E::T*)a.k, (const typename E::T*)a.v,
                      (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window,
+                     a.sink,
                      (float)((double)a.scale * 1.4426950408889634), n_qt);
   notify_launch("attn_fwd", 1, a.stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;

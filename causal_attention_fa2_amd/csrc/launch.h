@@ -24,7 +24,7 @@ struct Args {
   float* lse2;        // backward workspace: lse * log2(e), [B, Hq, Sq]
   float* part;        // backward workspace: fp32 dK / dV partial sums of the head-group parts
   int B, Hq, Hkv, Sq, Sk, D;  // Sq query rows, Sk >= Sq keys (queries: the last Sq positions)
-  int causal, window;
+  int causal, window, sink;  // sink: keys [0, sink) stay visible beside the window
   float scale;
   void* stream;
 };

@@ -17,6 +17,7 @@ measured and checked on; no dataset is involved, every input is synthetic):
   gqa64x8-q1024-k4096-d128  a prefill chunk: the last 1024 of 4096 positions (Sq=1024 queries,
                          Sk=4096 keys), otherwise as gqa64x8-s4096-d128
   gqa64x8-q1-k4096-d128  one decode query against 4096 cached keys, otherwise as above
+  swa-w1024-sink4-s8192  as swa-w1024-s8192 with the first 4 keys kept visible as sinks
 
 Draw order per workload: numpy.random.default_rng(seed); Q, K, V, dO as float32
 standard normals in that order (Q and dO with Sq rows, K and V with S rows) (dO then scaled by its standard deviation); then, for the
@@ -46,6 +47,7 @@ class Workload:
     do_std: float = 1.0
     head_factor: bool = False  # multiply Q and K per head by U(0.5, 2) factors
     Sq: int = 0  # query rows when fewer than the S keys (the last Sq positions); 0 = S
+    sink: int = 0  # leading keys that stay visible beside the window
 
     @property
     def scale(self) -> float:
@@ -72,6 +74,7 @@ WORKLOADS = {
                  do_std=0.1, Sq=1024),
         Workload("gqa64x8-q1-k4096-d128", 1, 64, 8, 4096, 128, "bf16", True, 0, 1007,
                  do_std=0.1, Sq=1),
+        Workload("swa-w1024-sink4-s8192", 1, 16, 16, 8192, 64, "bf16", True, 1024, 1008, sink=4),
     )
 }
 

@@ -13,17 +13,21 @@
  *   parameter switches between full-causal and sliding-window attention; the backward recomputes the
  *   softmax probabilities from the saved log-sum-exp; the kernel also takes fewer queries than keys
  *   (Sq <= Sk), for a prefill chunk or a one-token decode step against a cache.
+ *   "KYNETRA FOUNDRY" page, Vaultecho paragraph: beside the sliding window a few persistent sink
+ *   tokens at the start of the sequence stay attended.
  *
  * Definitions (for b < B, query head h < Hq, KV head g = h / (Hq / Hkv), rows i < Sq, keys j < Sk;
  * the queries are the last Sq positions, query i standing at p = i + Sk - Sq):
- *   visible(i, j) = (causal == 0 || j <= p) && (window == 0 || p - j < window)
+ *   visible(i, j) = (causal == 0 || j <= p) && (window == 0 || p - j < window || j < sink)
  *   x_ij   = scale * <Q[b,h,i,:], K[b,g,j,:]>            (visible j only)
  *   lse_i  = ln( sum_j exp(x_ij) )                       (natural log of the scaled scores)
  *   P_ij   = exp(x_ij - lse_i),  O_i = sum_j P_ij V[b,g,j,:]
  *   dQ_i   = scale * sum_j dS_ij K_j,  dK_j = scale * sum_{h in group(g)} sum_i dS_ij Q_i,
  *   dV_j   = sum_{h in group(g)} sum_i P_ij dO_i,  with dS_ij = P_ij (<dO_i, V_j> - <dO_i, O_i>).
  *   A window W >= 1 lets query i see keys p-W+1 .. p (W counts the diagonal). W = 0: no window.
- *   A single query (Sq = 1) sees every key causally, or the last W.
+ *   A single query (Sq = 1) sees every key causally, or the last W (plus the sink keys).
+ *   sink >= 0 counts the leading keys that stay visible once the window has moved past them; it only
+ *   matters with a window (without one every earlier key is visible anyway).
  *   attn_fwd / attn_bwd are the square case Sq = Sk = S of attn_fwd_qk / attn_bwd_qk.
  *
  * Layout: Q, O, dO, dQ are [B, Hq, Sq, D]; K, V, dK, dV are [B, Hkv, Sk, D]; lse is [B, Hq, Sq].
@@ -47,12 +51,12 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID = 1,     /* null pointer, size <= 0, Hq % Hkv != 0, window < 0, non-finite
-                               scale, workspace too small */
+  ATTN_ERR_INVALID = 1,     /* null pointer, size <= 0, Hq % Hkv != 0, window < 0, sink < 0,
+                               non-finite scale, workspace too small */
   ATTN_ERR_UNSUPPORTED = 2, /* D not 64 or 128, unknown dtype, window > 0 without causal,
                                Sq > Sk, B*Hq*Sq*D or B*Hkv*Sk*D >= 2^31 */
   ATTN_ERR_DEVICE = 3       /* the HIP runtime reported an error for a launch */
@@ -82,22 +86,24 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
              int B, int Hq, int Hkv, int S, int D, int causal, int window, float scale,
              void* stream);
 
-/* Forward with Sq queries against Sk >= Sq keys (bottom-right causal alignment, see above).
- * Reads q [B,Hq,Sq,D], k and v [B,Hkv,Sk,D]; writes o [B,Hq,Sq,D] and lse [B,Hq,Sq]. */
+/* Forward with Sq queries against Sk >= Sq keys (bottom-right causal alignment) and `sink` sink
+ * keys (see above). Reads q [B,Hq,Sq,D], k and v [B,Hkv,Sk,D]; writes o [B,Hq,Sq,D] and lse
+ * [B,Hq,Sq]. attn_fwd is this call with Sq = Sk = S and sink = 0. */
 int attn_fwd_qk(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
-                int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window,
+                int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, int sink,
                 float scale, void* stream);
 
 /* Workspace bytes of attn_bwd_qk: delta and lse * log2(e) (B*Hq*Sq fp32 each, 256-byte aligned)
  * and, when the head group is split, 2 * parts * B*Hkv*Sk*D fp32. 0 for rejected sizes. */
 size_t attn_bwd_qk_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D);
 
-/* Backward with Sq queries against Sk >= Sq keys. dout, dq are [B,Hq,Sq,D]; dk, dv [B,Hkv,Sk,D]
- * (keys no query sees get exact zeros). Same contract as attn_bwd otherwise. */
+/* Backward with Sq queries against Sk >= Sq keys and `sink` sink keys. dout, dq are
+ * [B,Hq,Sq,D]; dk, dv [B,Hkv,Sk,D] (keys no query sees get exact zeros). Same contract as
+ * attn_bwd otherwise; o and lse come from attn_fwd_qk with the same arguments. */
 int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const void* o,
                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
                 void* workspace, size_t workspace_bytes,
-                int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window,
+                int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, int sink,
                 float scale, void* stream);
 
 /* Optional launch observer, for profiling. When set, every entry point calls

@@ -33,16 +33,17 @@ def download(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def run_hip(q, k, v, do, dtype, causal=True, window=0, scale=None, want_bwd=True):
-    """Run attn_fwd (+ attn_bwd) on the GPU; returns numpy float64 arrays."""
+def run_hip(q, k, v, do, dtype, causal=True, window=0, scale=None, want_bwd=True, sink=0):
+    """Run attn_fwd (+ attn_bwd) -- their _qk forms for S_q < S_k or sink keys -- on the GPU;
+    returns numpy float64 arrays."""
     import torch
     import causal_attention_fa2_amd as fa
     tq, tk, tv = upload(q, dtype), upload(k, dtype), upload(v, dtype)
-    o, lse = fa.forward(tq, tk, tv, causal, window, scale)
+    o, lse = fa.forward(tq, tk, tv, causal, window, scale, sink=sink)
     out = {}
     if want_bwd:
         tdo = upload(do, dtype)
-        dq, dk, dv = fa.backward(tq, tk, tv, o, lse, tdo, causal, window, scale)
+        dq, dk, dv = fa.backward(tq, tk, tv, o, lse, tdo, causal, window, scale, sink=sink)
         torch.cuda.synchronize()
         out.update(dQ=download(dq), dK=download(dk), dV=download(dv))
         del tdo, dq, dk, dv

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fa.attn_abi_version() == 2
+    assert fa.attn_abi_version() == 3
     assert fa.attn_status_string(0) == "ok"
     assert fa.attn_status_string(1) == "invalid argument"
     assert fa.attn_status_string(2) == "unsupported configuration"
@@ -136,14 +136,14 @@ def test_bwd_validation(lib):
 
 
 def fwd_qk(lib, dtype=1, ptrs=(P, P, P, P, P), B=1, Hq=2, Hkv=2, Sq=16, Sk=64, D=64, causal=1,
-           window=0, scale=0.125):
-    return lib.attn_fwd_qk(dtype, *ptrs, B, Hq, Hkv, Sq, Sk, D, causal, window, scale, None)
+           window=0, scale=0.125, sink=0):
+    return lib.attn_fwd_qk(dtype, *ptrs, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, scale, None)
 
 
 def bwd_qk(lib, ws_bytes=0, ptrs=(P,) * 10, B=1, Hq=2, Hkv=2, Sq=16, Sk=64, D=64, causal=1,
-           window=0, scale=0.125, dtype=1):
-    return lib.attn_bwd_qk(dtype, *ptrs, ws_bytes, B, Hq, Hkv, Sq, Sk, D, causal, window, scale,
-                           None)
+           window=0, scale=0.125, dtype=1, sink=0):
+    return lib.attn_bwd_qk(dtype, *ptrs, ws_bytes, B, Hq, Hkv, Sq, Sk, D, causal, window, sink,
+                           scale, None)
 
 
 def test_qk_validation(lib):
@@ -155,6 +155,8 @@ def test_qk_validation(lib):
     assert fwd_qk(lib, Sq=0) == INV
     assert fwd_qk(lib, Sk=0) == INV
     assert fwd_qk(lib, Sq=65, Sk=64) == UNS        # more queries than keys is not defined
+    assert fwd_qk(lib, window=8, sink=-1) == INV
+    assert fwd_qk(lib, window=0, sink=-3) == INV
     assert fwd_qk(lib, Hq=3, Hkv=2) == INV
     assert fwd_qk(lib, causal=0, window=4) == UNS
     assert fwd_qk(lib, D=96) == UNS
@@ -169,6 +171,7 @@ def test_qk_validation(lib):
         assert bwd_qk(lib, need, ptrs=ptrs) == INV
     assert bwd_qk(lib, need - 1) == INV
     assert bwd_qk(lib, need, Sq=65) == UNS
+    assert bwd_qk(lib, need, window=4, sink=-1) == INV
     assert bwd_qk(lib, need, D=32) == UNS
 
 

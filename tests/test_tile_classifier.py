@@ -26,15 +26,20 @@ QK_LIST = [(1, 2), (1, 100), (1, 257), (5, 300), (31, 64), (33, 200), (64, 65), 
            (127, 300), (128, 256), (200, 257), (255, 300)]
 W_LIST = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 1024]
 TILES = [32, 64, 128]
+# (window, sink) pairs for the sink configurations
+SINK_LIST = [(1, 1), (2, 4), (31, 1), (33, 32), (64, 33), (65, 64), (100, 65), (1, 130), (128, 200), (32, 300)]
 
 
 def _configs():
     for sq, sk in [(S, S) for S in S_LIST] + QK_LIST:
         for br in TILES:
             for bc in TILES:
-                yield (sq, sk, br, bc, 0, 0)
+                yield (sq, sk, br, bc, 0, 0, 0)
                 for W in W_LIST:
-                    yield (sq, sk, br, bc, 1, W)
+                    yield (sq, sk, br, bc, 1, W, 0)
+                if sk >= 64:
+                    for W, n in SINK_LIST:
+                        yield (sq, sk, br, bc, 1, W, n)
 
 
 def test_tile_classifier_matches_mask(driver):
@@ -44,10 +49,10 @@ def test_tile_classifier_matches_mask(driver):
     lines = iter(out.splitlines())
     checked = 0
     for cfg in cfgs:
-        Sq, Sk, br, bc, causal, W = cfg
+        Sq, Sk, br, bc, causal, W, n_sink = cfg
         assert next(lines) == "CFG " + " ".join(map(str, cfg))
         nq, nk = -(-Sq // br), -(-Sk // bc)
-        m = oracle.visible_mask(np.arange(Sq), np.arange(Sk), bool(causal), W, Sk - Sq)
+        m = oracle.visible_mask(np.arange(Sq), np.arange(Sk), bool(causal), W, Sk - Sq, n_sink)
         # pad to whole tiles: out-of-range rows / keys are never visible
         P = np.zeros((nq * br, nk * bc), bool)
         P[:Sq, :Sk] = m
@@ -58,11 +63,13 @@ def test_tile_classifier_matches_mask(driver):
         all_vis = (blocks & inb.reshape(nq, br, nk, bc)).all(axis=(1, 3)) & \
             inb.reshape(nq, br, nk, bc).all(axis=(1, 3)) & blocks.all(axis=(1, 3))
         for qt in range(nq):
-            tag, q, lo, hi = next(lines).split()
+            tag, q, ns, lo, hi = next(lines).split()
             assert (tag, int(q)) == ("R", qt)
-            cols = np.nonzero(any_vis[qt])[0]
-            assert (int(lo), int(hi)) == (cols.min(), cols.max()), (cfg, qt)
-            assert np.all(any_vis[qt, cols.min():cols.max() + 1]), (cfg, qt)  # contiguous
+            ns, lo, hi = int(ns), int(lo), int(hi)
+            assert 0 <= ns and (ns == 0 or ns < lo) and lo <= hi, (cfg, qt)
+            listed = list(range(ns)) + list(range(lo, hi + 1))
+            # exactly the key tiles holding a visible pair: nothing missed, nothing extra
+            assert listed == list(np.nonzero(any_vis[qt])[0]), (cfg, qt)
         for kt in range(nk):
             tag, kk, lo, hi = next(lines).split()
             assert (tag, int(kk)) == ("C", kt)
