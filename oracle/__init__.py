@@ -8,3 +8,4 @@ from .attention import (  # noqa: F401
     rows_dq, rows_forward, visible_count, visible_mask,
 )
 from .compare import rel_l2  # noqa: F401
+from .paged import gather_sequence, paged_forward  # noqa: F401

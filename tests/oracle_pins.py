@@ -16,7 +16,10 @@ a transposed operand, an off-by-one mask -- fails at least one of them):
     lower-right causal bias, and a single decode query that sees every key (or the last W);
   * sink keys with a window: a decode query equals plain attention over the sink keys and the last
     W keys cut out and concatenated; sinks covering every key give plain causal attention; zero-query
-    counts are the size of the union of the window and the sink range.
+    counts are the size of the union of the window and the sink range;
+  * paged caches: an identity block layout reproduces the dense result exactly, shuffling the
+    physical blocks (with the table) changes no bit, sequences of different lengths equal their
+    own dense problems, and blocks shared by two sequences serve both.
 """
 from __future__ import annotations
 
@@ -527,6 +530,64 @@ def pin_sink_helpers(A):
     assert np.max(np.abs(dv - r["dV"][0, 0, cols])) <= 1e-13
 
 
+# ---------------------------------------------------------------- paged K/V cache
+def _pool_from_dense(kd, bs, extra, rng, perm=True):
+    """Lay a dense [B, Hkv, S, D] tensor out as a pool of bs-token blocks (B * ceil(S/bs) blocks
+    in a shuffled order, plus `extra` blocks of noise) and return (pool, table)."""
+    B, Hkv, S, D = kd.shape
+    nper = -(-S // bs)
+    nb = B * nper + extra
+    order = rng.permutation(nb) if perm else np.arange(nb)
+    pool = rng.standard_normal((nb, Hkv, bs, D))
+    table = np.full((B, nper + 2), -7, dtype=np.int64)  # trailing entries are never read
+    for b in range(B):
+        for t in range(nper):
+            phys = order[b * nper + t]
+            table[b, t] = phys
+            n = min(bs, S - t * bs)
+            pool[phys, :, :n, :] = kd[b, :, t * bs:t * bs + n, :]
+    return pool, table
+
+
+def pin_paged_matches_dense(A):
+    """An identity layout and a shuffled layout of the same dense K/V both give the dense result."""
+    import oracle.paged as PG
+    rng = np.random.default_rng(41)
+    q, k, v, _ = _rng_inputs(41, 2, 4, 2, 5, 8, Sk=37)
+    O, L = A.forward(q, k, v, True, 9, 0.5, sink=2)
+    for bs, perm in ((16, False), (16, True), (4, True), (64, True)):
+        kp, table = _pool_from_dense(k, bs, 3, np.random.default_rng(bs), perm)
+        vp, table2 = _pool_from_dense(v, bs, 3, np.random.default_rng(bs), perm)
+        assert np.array_equal(table, table2)
+        Op, Lp = PG.paged_forward(q, kp, vp, table, np.array([37, 37]), True, 9, 0.5, sink=2)
+        assert np.array_equal(Op, O) and np.array_equal(Lp, L), (bs, perm)
+
+
+def pin_paged_lengths_and_sharing(A):
+    """Sequences of different lengths equal their own dense problems; two sequences whose tables
+    share blocks read the same keys."""
+    import oracle.paged as PG
+    rng = np.random.default_rng(42)
+    bs, D, Hkv = 8, 4, 2
+    pool_k = rng.standard_normal((12, Hkv, bs, D))
+    pool_v = rng.standard_normal((12, Hkv, bs, D))
+    table = np.array([[3, 7, 1, 0], [3, 7, 9, 11]])  # the first 16 tokens are shared
+    lens = np.array([21, 30])
+    q = rng.standard_normal((2, 4, 3, D))
+    O, L = PG.paged_forward(q, pool_k, pool_v, table, lens, True, 0, 0.7)
+    for b in range(2):
+        blocks = table[b]
+        kd = np.concatenate([pool_k[p] for p in blocks], axis=1)[:, :lens[b]]
+        vd = np.concatenate([pool_v[p] for p in blocks], axis=1)[:, :lens[b]]
+        o, lse = A.forward(q[b:b + 1], kd[None], vd[None], True, 0, 0.7)
+        assert np.array_equal(O[b], o[0]) and np.array_equal(L[b], lse[0]), b
+    # changing a block only the second sequence uses leaves the first bitwise unchanged
+    pool_k2 = pool_k.copy()
+    pool_k2[9] += 1.0
+    O2, L2 = PG.paged_forward(q, pool_k2, pool_v, table, lens, True, 0, 0.7)
+    assert np.array_equal(O2[0], O[0]) and not np.array_equal(O2[1], O[1])
+
+
 ALL_PINS = [
     pin_fd_every_entry, pin_bruteforce, pin_torch_sdpa, pin_three_token_closed_form,
     pin_constant_v, pin_identical_keys, pin_window_one, pin_zero_queries, pin_rows_sum_to_one,
@@ -534,5 +595,5 @@ ALL_PINS = [
     pin_row_and_column_helpers, pin_chunk_is_suffix_of_square, pin_torch_lower_right_causal,
     pin_single_decode_query, pin_chunk_helpers, pin_sink_decode_is_concatenation,
     pin_sinks_covering_all_keys, pin_sink_zero_query_counts, pin_sink_chunk_is_suffix_of_square,
-    pin_sink_helpers,
+    pin_sink_helpers, pin_paged_matches_dense, pin_paged_lengths_and_sharing,
 ]

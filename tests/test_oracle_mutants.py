@@ -11,6 +11,8 @@ import oracle_pins as P
 _real_head_rows = A.head_rows
 _real_fb = A.forward_backward
 _real_mask = A.visible_mask
+import oracle.paged as PG  # noqa: E402
+_real_gather = PG.gather_sequence
 
 
 def _head_rows_mut(kind):
@@ -73,6 +75,20 @@ def _mask_mut(kind):
     return f
 
 
+def _gather_mut(kind):
+    def f(pool, block_table, b, n_tokens, block_size):
+        nb, Hkv, bs, D = pool.shape
+        out = np.empty((Hkv, n_tokens, D))
+        for t in range(n_tokens):
+            if kind == "paged_slot_reversed":
+                phys, slot = int(block_table[b, t // bs]), bs - 1 - t % bs
+            else:  # "paged_table_of_sequence_0"
+                phys, slot = int(block_table[0, t // bs]), t % bs
+            out[:, t, :] = pool[phys, :, slot, :]
+        return out
+    return f
+
+
 MUTANTS = {
     "dropped_delta": ("head_rows", _head_rows_mut("dropped_delta")),
     "dS_sign": ("head_rows", _head_rows_mut("dS_sign")),
@@ -89,6 +105,8 @@ MUTANTS = {
     "sink_ignored": ("visible_mask", _mask_mut("sink_ignored")),
     "sink_off_by_one": ("visible_mask", _mask_mut("sink_off_by_one")),
     "sink_without_causal": ("visible_mask", _mask_mut("sink_without_causal")),
+    "paged_slot_reversed": ("paged.gather_sequence", _gather_mut("paged_slot_reversed")),
+    "paged_table_of_sequence_0": ("paged.gather_sequence", _gather_mut("paged_table_of_sequence_0")),
 }
 
 # Pins that run quickly enough to try on every mutant.
@@ -98,7 +116,10 @@ FAST_PINS = [p for p in P.ALL_PINS if p is not P.pin_torch_sdpa] + [P.pin_torch_
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
-    monkeypatch.setattr(A, attr, fn)
+    if attr.startswith("paged."):
+        monkeypatch.setattr(PG, attr.split(".", 1)[1], fn)
+    else:
+        monkeypatch.setattr(A, attr, fn)
     if attr == "forward_backward":
         # forward/backward/... reach forward_backward through the module, so they see it too
         pass
