@@ -148,6 +148,69 @@ def cpu_baseline(w, q, k, v, do, heads: int):
             "cpu_model": model, "blas": blas}
 
 
+def bench_paged(w, args, torch, fa) -> int:
+    """Forward against a paged cache (attn_fwd_paged): a step is one forward over the batch."""
+    import numpy as np
+    from causal_attention_fa2_amd.workloads import make_inputs, paged_layout
+    q, k, v, _ = make_inputs(w)
+    kp, vp, table, lens = paged_layout(w, k, v)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    tq, tkp, tvp = (torch.from_numpy(x).to(td).cuda() for x in (q, kp, vp))
+    tt, tl = torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
+    Sq = w.n_q
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.Hq, Sq), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.attn_fwd_paged(tq, tkp, tvp, tt, tl, o, lse, w.causal, w.window, w.scale, None, w.sink)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream()
+    evs = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    kms = sorted(a.elapsed_time(b) for a, b in evs)
+    kmed = kms[len(kms) // 2]
+    eb = 2 if w.dtype == "bf16" else 4
+    pairs = sum(attended_pairs(int(n), w.causal, w.window, Sq, w.sink) for n in lens)
+    flops = 4.0 * w.Hq * pairs * w.D
+    kv_bytes = float(sum(2 * w.Hkv * int(n) * w.D * eb for n in lens))
+    qo_bytes = 2.0 * w.B * w.Hq * Sq * w.D * eb + 4.0 * w.B * w.Hq * Sq
+    value = flops / (ms * 1e-3) / 1e12
+    gbs = (kv_bytes + qo_bytes) / (kmed * 1e-3) / 1e9
+    out = {
+        "metric": f"paged-cache attention forward TFLOP/s ({w.name})", "value": round(value, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": Sq, "S_max": w.S,
+                   "D": w.D, "block": w.paged, "keys_total": int(lens.sum()), "causal": w.causal,
+                   "window": w.window, "parallelism": "none (1 GPU)"},
+        "kernel_ms_median": round(kmed, 4),
+        "roofline": {"kernel": "attn_fwd", "bound": "hbm" if Sq * (w.Hq // w.Hkv) <= 64 else "mfma",
+                     "achieved": round(gbs, 1) if Sq * (w.Hq // w.Hkv) <= 64 else
+                     round(flops / (kmed * 1e-3) / 1e12, 1),
+                     "peak": PEAK_HBM_GBS if Sq * (w.Hq // w.Hkv) <= 64 else PEAK_BF16_TFLOPS,
+                     "unit": "GB/s" if Sq * (w.Hq // w.Hkv) <= 64 else "TFLOP/s", "traffic": None},
+    }
+    r = out["roofline"]
+    r["frac"] = round(r["achieved"] / r["peak"], 4)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +248,8 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if w.paged:
+        return bench_paged(w, args, torch, fa)
     q, k, v, do = make_inputs(w)
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     tq, tk, tv, tdo = (torch.from_numpy(x).to(td).cuda() for x in (q, k, v, do))

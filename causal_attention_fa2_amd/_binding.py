@@ -53,6 +53,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_qk.restype = i
     lib.attn_bwd_qk_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i,
+                                   f, vp]
+    lib.attn_fwd_paged.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -163,6 +166,32 @@ def attn_fwd_qk(q, k, v, o, lse, causal: bool = True, window: int = 0, scale: fl
                                     _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_qk")
+
+
+def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlen_k, o, lse, causal: bool = True,
+                   window: int = 0, scale: float | None = None, stream=None, sink: int = 0) -> None:
+    """Calls attn_fwd_paged: q [B,Hq,Sq,D]; k_pool/v_pool [num_blocks,Hkv,block_size,D] (q's
+    dtype); block_table int32 [B, max_blocks]; seqlen_k int32 [B] -> o [B,Hq,Sq,D], lse [B,Hq,Sq]."""
+    import torch
+    if not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous GPU tensor")
+    B, Hq, Sq, D = q.shape
+    nb, Hkv, bs = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    _check_tensor("k_pool", k_pool, (nb, Hkv, bs, D), q.dtype, q.device)
+    _check_tensor("v_pool", v_pool, (nb, Hkv, bs, D), q.dtype, q.device)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _check_tensor("block_table", block_table, tuple(block_table.shape), torch.int32, q.device)
+    _check_tensor("seqlen_k", seqlen_k, (B,), torch.int32, q.device)
+    _check_tensor("o", o, (B, Hq, Sq, D), q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, Sq), torch.float32, q.device)
+    scale = D ** -0.5 if scale is None else float(scale)
+    st = load_library().attn_fwd_paged(
+        _dtype_code(q), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+        seqlen_k.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Sq, D, bs,
+        block_table.shape[1], nb, int(bool(causal)), int(window), int(sink), scale, _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_paged")
 
 
 def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale):

@@ -8,7 +8,8 @@
 // narrows causal attention); with fewer queries than keys the queries are the last Sq positions
 // (same section: one kernel for prefill and for one-token decode against a cache), and more
 // queries than keys is not defined; sink keys ("KYNETRA FOUNDRY", Vaultecho paragraph) are a count
-// >= 0 of leading keys that stay visible beside the window.
+// >= 0 of leading keys that stay visible beside the window; a paged cache ("KYNETRA FOUNDRY",
+// paged-KV paragraph) uses power-of-two blocks of at least 16 tokens.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -140,6 +141,47 @@ int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void*
              float scale, void* stream) {
   return attn_bwd_qk(dtype, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq,
                      Hkv, S, S, D, causal, window, 0, scale, stream);
+}
+
+int attn_fwd_paged(int dtype, const void* q, const void* k_pool, const void* v_pool,
+                   const int* block_table, const int* seqlen_k, void* o, float* lse, int B, int Hq,
+                   int Hkv, int Sq, int D, int block_size, int max_blocks, int num_blocks,
+                   int causal, int window, int sink, float scale, void* stream) {
+  if (!q || !k_pool || !v_pool || !block_table || !seqlen_k || !o || !lse) return ATTN_ERR_INVALID;
+  if (block_size <= 0 || max_blocks <= 0 || num_blocks <= 0) return ATTN_ERR_INVALID;
+  if ((block_size & (block_size - 1)) != 0 || block_size < 16 || block_size > (1 << 20))
+    return ATTN_ERR_UNSUPPORTED;
+  const int64_t capacity = (int64_t)max_blocks * block_size;  // keys one sequence can hold
+  if (capacity >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  // Sk = Sq here only for the shared checks; each sequence's own Sk comes from seqlen_k
+  int st = check_common(dtype, B, Hq, Hkv, Sq, Sq, D, causal, window, sink, scale);
+  if (st != ATTN_OK) return st;
+  if (Sq > capacity) return ATTN_ERR_UNSUPPORTED;
+  fa::Args a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Sk = Sq;  // replaced per sequence on the device
+  a.D = D;
+  a.causal = causal;
+  a.window = window;
+  a.sink = sink;
+  a.scale = scale;
+  a.stream = stream;
+  a.paged = true;
+  a.pg.table = block_table;
+  a.pg.seqlen = seqlen_k;
+  a.pg.shift = __builtin_ctz((unsigned)block_size);
+  a.pg.max_blocks = max_blocks;
+  a.pg.num_blocks = num_blocks;
+  return fa::launch_fwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
 const char* attn_status_string(int status) {

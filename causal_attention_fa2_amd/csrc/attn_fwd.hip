@@ -26,12 +26,15 @@
 
 namespace fa {
 
-template <class E, int D, int NW, int KB, int NST>
+// PG: K and V are pools of a paged cache read through pg (page "KYNETRA FOUNDRY", paged-KV
+// paragraph: a per-sequence block table maps token positions to pool blocks); S is then the
+// sequence's own key count.
+template <class E, int D, int NW, int KB, int NST, bool PG>
 __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
     int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale_log2,
-    int n_qt) {
+    int n_qt, PagedKV pg) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 32 * KB;
   constexpr int DS = D / 16;  // 16-wide contraction steps over the head dimension
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   const int g = bg - b * Hkv;
   const int h = g * G + hh;
 
+  if constexpr (PG) S = imin_(imax_(pg.seqlen[b], Sq), pg.max_blocks << pg.shift);
   const int off = S - Sq;  // query row r stands at key position r + off
   const typename E::T* q_bh = Q + (size_t)(b * Hq + h) * Sq * D;
   const typename E::T* k_bg = K + (size_t)bg * S * D;
@@ -79,8 +83,14 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
 
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
     const int j0 = tile_of(s) * BC;
-    dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
-    dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
+    if constexpr (PG) {
+      const int* tab = pg.table + (size_t)b * pg.max_blocks;
+      dma_tile_paged<E, BC, D, NW>(stg, K, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
+      dma_tile_paged<E, BC, D, NW>(stg + KvTile::kBytes, V, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
+    } else {
+      dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
+      dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
+    }
   };
   issue(0, ring);
   if (NST == 3 && n_steps > 1) issue(1, ring + kStage);
@@ -217,12 +227,12 @@ static int launch_fwd_t(const Args& a) {
   constexpr int NST = E::kBytes == 2 ? kFwdStages : 3;
   const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
   dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
+  const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   notify_launch("attn_fwd", 0, a.stream);
-  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NST>), grid, block, 0, (hipStream_t)a.stream,
-                     (const typename E::T*)a.q, (const typename E::T*)a.k, (const typename E::T*)a.v,
-                     (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window,
-                     a.sink,
-                     (float)((double)a.scale * 1.4426950408889634), n_qt);
+  auto kern = a.paged ? fwd_kernel<E, D, NW, KB, NST, true> : fwd_kernel<E, D, NW, KB, NST, false>;
+  hipLaunchKernelGGL(kern, grid, block, 0, (hipStream_t)a.stream, (const typename E::T*)a.q,
+                     (const typename E::T*)a.k, (const typename E::T*)a.v, (typename E::T*)a.o, a.lse,
+                     a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, scale_log2, n_qt, a.pg);
   notify_launch("attn_fwd", 1, a.stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

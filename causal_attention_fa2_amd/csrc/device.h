@@ -360,6 +360,46 @@ __device__ __forceinline__ void dma_tile(char* lds, const typename E::T* __restr
 template <class E, int ROWS, int D, int NW>
 constexpr int dma_tile_ops() { return LdsTile<E, ROWS, D>::kBytes / 1024 / NW; }
 
+// The same copy from a paged cache: row t of the sequence lives in physical block tab[t >> shift]
+// of a [nblocks, Hkv, 2^shift, D] pool, head g, slot t & (2^shift - 1). Block sizes are powers of
+// two >= 16 and row0 is a multiple of ROWS, so the tile spans at most max(1, ROWS >> shift) <= 4
+// blocks; their table entries are wave-uniform (scalar loads). Table indices are clamped to the
+// entries that cover rows [0, S) and physical blocks to [0, nblocks): malformed tables cannot
+// make the copy leave the pool. Rows at or past S are read from row S - 1, as in dma_tile.
+template <class E, int ROWS, int D, int NW>
+__device__ __forceinline__ void dma_tile_paged(char* lds, const typename E::T* __restrict__ pool,
+                                               const int* __restrict__ tab, int g, int Hkv, int shift,
+                                               int nblocks, int row0, int S) {
+  typedef LdsTile<E, ROWS, D> Tile;
+  constexpr int kBlocks = Tile::kBytes / 1024;
+  static_assert(kBlocks % NW == 0, "tile must split into whole 1 KB blocks per wave");
+  static_assert(ROWS <= 64, "at most 4 pool blocks of 16 rows per tile");
+  const int lane = lane_id();
+  const int w = wave_id();
+  const uint32_t base = lds_addr(lds);
+  const int lb0 = row0 >> shift;
+  const int lb_last = (S - 1) >> shift;
+  int ph[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lb = imin_(lb0 + i, lb_last);
+    ph[i] = imin_(imax_(tab[lb], 0), nblocks - 1);
+  }
+#pragma unroll
+  for (int n = 0; n < kBlocks / NW; ++n) {
+    const int blk = n * NW + w;
+    const int c = blk * 64 + lane;
+    const int r = c / Tile::kChunks;
+    const int pos = c % Tile::kChunks;
+    const int gr = imin_(row0 + r, S - 1);
+    const int rel = (gr >> shift) - lb0;  // 0 .. 3
+    const int phys = rel == 0 ? ph[0] : (rel == 1 ? ph[1] : (rel == 2 ? ph[2] : ph[3]));
+    const size_t row = ((((size_t)phys * Hkv + g) << shift) | (size_t)(gr & ((1 << shift) - 1)));
+    const char* gp = reinterpret_cast<const char*>(pool + row * D) + ((pos ^ Tile::swz(r)) << 4);
+    dma16(gp, base + blk * 1024);
+  }
+}
+
 // 64 consecutive floats src[clamp(i0 + lane)] -> lds[0..63] (one wave, one instruction).
 __device__ __forceinline__ void dma_row_floats(char* lds, const float* __restrict__ src, int i0, int S) {
   const int r = imin_(i0 + lane_id(), S - 1);

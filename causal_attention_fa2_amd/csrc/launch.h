@@ -8,6 +8,16 @@ namespace fa {
 
 enum { kF32 = 0, kBF16 = 1 };
 
+// K / V in a paged cache: pools [num_blocks, Hkv, 2^shift, D]; logical block t of sequence b is
+// pool block table[b * max_blocks + t]; sequence b has seqlen[b] keys (device arrays).
+struct PagedKV {
+  const int* table;
+  const int* seqlen;
+  int shift;
+  int max_blocks;
+  int num_blocks;
+};
+
 struct Args {
   int dtype;
   const void* q;
@@ -27,6 +37,8 @@ struct Args {
   int causal, window, sink;  // sink: keys [0, sink) stay visible beside the window
   float scale;
   void* stream;
+  bool paged;  // forward only: k, v are pools read through pg (Sk is then per sequence)
+  PagedKV pg;
 };
 
 // Tells the launch observer (attn_set_launch_hook) that `kernel` is about to be / has been

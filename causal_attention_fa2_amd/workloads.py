@@ -18,6 +18,10 @@ measured and checked on; no dataset is involved, every input is synthetic):
                          Sk=4096 keys), otherwise as gqa64x8-s4096-d128
   gqa64x8-q1-k4096-d128  one decode query against 4096 cached keys, otherwise as above
   swa-w1024-sink4-s8192  as swa-w1024-s8192 with the first 4 keys kept visible as sinks
+  paged-decode-b16-gqa64x8  16 sequences of U[1024, 8192] cached keys in 16-token pool blocks,
+                         one decode query each (forward only), Hq=64, Hkv=8, D=128, bf16
+  paged-chunk-b4-q512-gqa64x8  4 sequences of U[2048, 8192] keys in 64-token blocks, a 512-query
+                         prefill chunk each (forward only)
 
 Draw order per workload: numpy.random.default_rng(seed); Q, K, V, dO as float32
 standard normals in that order (Q and dO with Sq rows, K and V with S rows) (dO then scaled by its standard deviation); then, for the
@@ -48,6 +52,8 @@ class Workload:
     head_factor: bool = False  # multiply Q and K per head by U(0.5, 2) factors
     Sq: int = 0  # query rows when fewer than the S keys (the last Sq positions); 0 = S
     sink: int = 0  # leading keys that stay visible beside the window
+    paged: int = 0  # > 0: K/V in a paged pool of blocks of this many tokens (forward only)
+    len_min: int = 0  # paged: sequence b holds U[len_min, S] keys
 
     @property
     def scale(self) -> float:
@@ -75,6 +81,10 @@ WORKLOADS = {
         Workload("gqa64x8-q1-k4096-d128", 1, 64, 8, 4096, 128, "bf16", True, 0, 1007,
                  do_std=0.1, Sq=1),
         Workload("swa-w1024-sink4-s8192", 1, 16, 16, 8192, 64, "bf16", True, 1024, 1008, sink=4),
+        Workload("paged-decode-b16-gqa64x8", 16, 64, 8, 8192, 128, "bf16", True, 0, 1009, Sq=1,
+                 paged=16, len_min=1024),
+        Workload("paged-chunk-b4-q512-gqa64x8", 4, 64, 8, 8192, 128, "bf16", True, 0, 1010, Sq=512,
+                 paged=64, len_min=2048),
     )
 }
 
@@ -130,6 +140,32 @@ def make_inputs(w: Workload, *, seed: int | None = None, B: int | None = None,
         q *= cq[None, :, None, None]
         k *= ck[None, :, None, None]
     return tuple(to_elem(t, w.dtype) for t in (q, k, v, do))
+
+
+def paged_layout(w: Workload, k: np.ndarray, v: np.ndarray):
+    """Sequence lengths and a paged layout of k / v for a paged workload: (k_pool, v_pool, table,
+    lens). Lengths are U[len_min, S] (seeded); the first lens[b] keys of sequence b go to
+    ceil(lens[b] / block) pool blocks in a seeded random order; the table rows are padded with 0."""
+    rng = np.random.default_rng(w.seed + 7919)
+    lens = rng.integers(w.len_min, w.S + 1, size=w.B).astype(np.int32)
+    lens = np.maximum(lens, w.n_q)
+    bs = w.paged
+    need = [-(-int(n) // bs) for n in lens]
+    nb = sum(need)
+    order = rng.permutation(nb)
+    kp = np.zeros((nb, w.Hkv, bs, w.D), np.float32)
+    vp = np.zeros((nb, w.Hkv, bs, w.D), np.float32)
+    table = np.zeros((w.B, max(need)), np.int32)
+    i = 0
+    for b in range(w.B):
+        for t in range(need[b]):
+            phys = order[i]
+            i += 1
+            table[b, t] = phys
+            n = min(bs, int(lens[b]) - t * bs)
+            kp[phys, :, :n] = k[b, :, t * bs:t * bs + n]
+            vp[phys, :, :n] = v[b, :, t * bs:t * bs + n]
+    return kp, vp, table, lens
 
 
 def random_tensor(shape, dtype: str, seed: int, std: float = 1.0) -> np.ndarray:

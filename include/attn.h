@@ -14,7 +14,9 @@
  *   softmax probabilities from the saved log-sum-exp; the kernel also takes fewer queries than keys
  *   (Sq <= Sk), for a prefill chunk or a one-token decode step against a cache.
  *   "KYNETRA FOUNDRY" page, Vaultecho paragraph: beside the sliding window a few persistent sink
- *   tokens at the start of the sequence stay attended.
+ *   tokens at the start of the sequence stay attended. Same page, paged-KV paragraph: a sequence's
+ *   K/V cache lives in fixed-size blocks anywhere in a global pool, found through a per-sequence
+ *   block table (attn_fwd_paged).
  *
  * Definitions (for b < B, query head h < Hq, KV head g = h / (Hq / Hkv), rows i < Sq, keys j < Sk;
  * the queries are the last Sq positions, query i standing at p = i + Sk - Sq):
@@ -51,14 +53,15 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, size <= 0, Hq % Hkv != 0, window < 0, sink < 0,
                                non-finite scale, workspace too small */
   ATTN_ERR_UNSUPPORTED = 2, /* D not 64 or 128, unknown dtype, window > 0 without causal,
-                               Sq > Sk, B*Hq*Sq*D or B*Hkv*Sk*D >= 2^31 */
+                               Sq > Sk, B*Hq*Sq*D or B*Hkv*Sk*D >= 2^31, a paged block size
+                               that is not a power of two in [16, 2^20] */
   ATTN_ERR_DEVICE = 3       /* the HIP runtime reported an error for a launch */
 } attn_status_t;
 
@@ -105,6 +108,21 @@ int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const vo
                 void* workspace, size_t workspace_bytes,
                 int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, int sink,
                 float scale, void* stream);
+
+/* Forward against a paged K/V cache. k_pool and v_pool are [num_blocks, Hkv, block_size, D]
+ * (dtype); block_table is int32 [B, max_blocks]: logical block t of sequence b (its tokens
+ * t*block_size .. +block_size-1) is pool block block_table[b*max_blocks + t]; seqlen_k is int32
+ * [B]: sequence b has seqlen_k[b] keys, and its Sq queries are its last Sq positions
+ * (p = i + seqlen_k[b] - Sq; causal, window and sink as above). q, o are [B,Hq,Sq,D], lse
+ * [B,Hq,Sq]. block_size is a power of two >= 16. The table and lengths are device arrays that
+ * the host does not read: a length outside [Sq, max_blocks*block_size] is clamped into it and a
+ * table entry outside [0, num_blocks) is clamped into it, so a malformed table cannot make the
+ * kernel read outside the pools (the results are then unspecified). Blocks may be shared
+ * between sequences (read-only here). */
+int attn_fwd_paged(int dtype, const void* q, const void* k_pool, const void* v_pool,
+                   const int* block_table, const int* seqlen_k, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Sq, int D, int block_size, int max_blocks,
+                   int num_blocks, int causal, int window, int sink, float scale, void* stream);
 
 /* Optional launch observer, for profiling. When set, every entry point calls
  * hook(kernel, 0, stream, user) just before and hook(kernel, 1, stream, user) just after it

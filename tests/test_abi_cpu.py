@@ -31,8 +31,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_qk", "attn_bwd_qk_workspace_bytes",
-                     "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_qk", "attn_set_launch_hook",
-                     "attn_status_string"]
+                     "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_paged", "attn_fwd_qk",
+                     "attn_set_launch_hook", "attn_status_string"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (attn_\w+)", out))
@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fa.attn_abi_version() == 3
+    assert fa.attn_abi_version() == 4
     assert fa.attn_status_string(0) == "ok"
     assert fa.attn_status_string(1) == "invalid argument"
     assert fa.attn_status_string(2) == "unsupported configuration"
@@ -173,6 +173,32 @@ def test_qk_validation(lib):
     assert bwd_qk(lib, need, Sq=65) == UNS
     assert bwd_qk(lib, need, window=4, sink=-1) == INV
     assert bwd_qk(lib, need, D=32) == UNS
+
+
+def fwd_paged(lib, dtype=1, ptrs=(P,) * 7, B=2, Hq=4, Hkv=2, Sq=1, D=128, bs=16, max_blocks=8,
+              num_blocks=20, causal=1, window=0, sink=0, scale=0.125):
+    return lib.attn_fwd_paged(dtype, *ptrs, B, Hq, Hkv, Sq, D, bs, max_blocks, num_blocks, causal,
+                              window, sink, scale, None)
+
+
+def test_paged_validation(lib):
+    INV, UNS = fa.ATTN_ERR_INVALID, fa.ATTN_ERR_UNSUPPORTED
+    for i in range(7):
+        ptrs = [P] * 7
+        ptrs[i] = None
+        assert fwd_paged(lib, ptrs=ptrs) == INV
+    assert fwd_paged(lib, bs=0) == INV
+    assert fwd_paged(lib, max_blocks=0) == INV
+    assert fwd_paged(lib, num_blocks=0) == INV
+    assert fwd_paged(lib, bs=24) == UNS            # not a power of two
+    assert fwd_paged(lib, bs=8) == UNS             # below 16
+    assert fwd_paged(lib, bs=1 << 21) == UNS
+    assert fwd_paged(lib, bs=1 << 20, max_blocks=1 << 11) == UNS  # 2^31 keys per sequence
+    assert fwd_paged(lib, Sq=129, bs=16, max_blocks=8) == UNS     # more queries than any sequence holds
+    assert fwd_paged(lib, Hq=3) == INV
+    assert fwd_paged(lib, sink=-1, window=4) == INV
+    assert fwd_paged(lib, causal=0, window=4) == UNS
+    assert fwd_paged(lib, D=96) == UNS
 
 
 def test_launch_hook_set_and_clear(lib):
