@@ -24,6 +24,10 @@ What it computes is plain materialised softmax attention and its exact gradient,
     a single-token decode against a cache.
   * "KYNETRA FOUNDRY" page, Vaultecho paragraph: besides the sliding window of recent tokens a few
     persistent "sink" tokens at the start of the sequence stay attended.
+  * "Build a standalone, production grade system that trains a 4,..." (the page-4 prompt), its
+    curriculum section: documents are concatenated contiguously into fixed-length buffers with
+    document-boundary index arrays and boundary reset indicators, and the pipeline generates the
+    matching attention block masks.
 
 Readings where the pages leave a step open (each also listed in the design notes):
   * tensors are [B, H, S, D] contiguous, D fastest; K and V have Hkv heads, Q/O/dO have Hq heads;
@@ -39,6 +43,9 @@ Readings where the pages leave a step open (each also listed in the design notes
   * sinks: the first n_sink keys stay visible to every query at or after them even when the window
     has moved past them (key j visible iff causal allows it and (p - j < W or j < n_sink)); without a
     window every earlier key is visible anyway, so n_sink only matters when W > 0;
+  * packed documents: cu_seqlens[b] = (0 = c_0 <= c_1 <= ... <= c_n = S) splits batch row b into
+    documents [c_k, c_{k+1}); key j is visible to query i only if both lie in the same document
+    (attention is reset at every boundary), on top of the causal mask and window;
   * every row has at least one visible key (its own position), so no empty-row convention is needed.
 
 Rows are processed in blocks of `row_block` queries only to bound memory: each row's softmax is
@@ -52,7 +59,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "kv_head", "visible_mask", "visible_count", "head_rows", "forward", "backward",
+    "kv_head", "document_of", "visible_mask", "visible_count", "head_rows", "forward", "backward",
     "forward_backward", "probabilities", "rows_forward", "rows_dq", "cols_dkdv",
 ]
 
@@ -84,9 +91,17 @@ def kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def visible_mask(rows, cols, causal: bool, window: int, offset: int = 0, sink: int = 0) -> np.ndarray:
+def document_of(pos, cu) -> np.ndarray:
+    """Document index of each position: the k with cu[k] <= pos < cu[k+1]."""
+    cu = np.asarray(cu, dtype=np.int64)
+    return np.searchsorted(cu, np.asarray(pos, dtype=np.int64), side="right") - 1
+
+
+def visible_mask(rows, cols, causal: bool, window: int, offset: int = 0, sink: int = 0,
+                 docs=None) -> np.ndarray:
     """Boolean [len(rows), len(cols)]: with query i at position p = i + offset, key j is visible
-    iff (not causal or j <= p) and (window == 0 or p - j < window or j < sink).
+    iff (not causal or j <= p) and (window == 0 or p - j < window or j < sink) and, when docs
+    (one batch row's cu_seqlens) is given, p and j lie in the same document.
     offset = S_k - S_q; sink = number of sink keys."""
     i = np.asarray(rows, dtype=np.int64)[:, None] + offset
     j = np.asarray(cols, dtype=np.int64)[None, :]
@@ -95,6 +110,8 @@ def visible_mask(rows, cols, causal: bool, window: int, offset: int = 0, sink: i
         m &= j <= i
     if window > 0:
         m &= ((i - j) < window) | (j < sink)
+    if docs is not None:
+        m &= document_of(i, docs) == document_of(j, docs)
     return m
 
 
@@ -103,7 +120,7 @@ def visible_count(i: int, S: int, causal: bool, window: int, offset: int = 0, si
     return int(visible_mask([i], np.arange(S), causal, window, offset, sink).sum())
 
 
-def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0, sink=0):
+def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0, sink=0, docs=None):
     """One head, a set of query rows, all S_k keys.
 
     qh [S_q, D], kh/vh [S_k, D], doh [S_q, D] or None (float64); query i at position i + offset.
@@ -111,7 +128,7 @@ def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0, sink=
     LSE [R], and when doh is given dP [R, S_k], delta [R] and dS [R, S_k]."""
     S = kh.shape[0]
     rows = np.asarray(rows, dtype=np.int64)
-    mask = visible_mask(rows, np.arange(S), causal, window, offset, sink)
+    mask = visible_mask(rows, np.arange(S), causal, window, offset, sink, docs)
     x = scale * (qh[rows] @ kh.T)                     # scaled scores
     x = np.where(mask, x, -np.inf)
     m = x.max(axis=1, keepdims=True)                  # finite: the row's own position is visible
@@ -132,10 +149,12 @@ def _f64(*xs):
     return tuple(np.asarray(x, dtype=np.float64) for x in xs)
 
 
-def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256, sink=0):
+def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256, sink=0,
+                     cu_seqlens=None):
     """Full attention forward (O, LSE) and, when do is given, backward (dQ, dK, dV).
 
-    q, do [B,Hq,S_q,D]; k, v [B,Hkv,S_k,D] with S_q <= S_k. Returns float64 arrays in a dict."""
+    q, do [B,Hq,S_q,D]; k, v [B,Hkv,S_k,D] with S_q <= S_k; cu_seqlens [B, n+1] document
+    boundaries (optional). Returns float64 arrays in a dict."""
     B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
     off = Sk - S
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
@@ -155,7 +174,8 @@ def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_bl
             for r0 in range(0, S, row_block):
                 rows = np.arange(r0, min(S, r0 + row_block))
                 t = head_rows(q[b, h], k[b, g], v[b, g], rows, causal, window, scale,
-                              None if do is None else do[b, h], off, sink)
+                              None if do is None else do[b, h], off, sink,
+                              None if cu_seqlens is None else cu_seqlens[b])
                 O[b, h, rows] = t["O"]
                 LSE[b, h, rows] = t["LSE"]
                 if do is not None:
@@ -166,15 +186,15 @@ def forward_backward(q, k, v, do=None, causal=True, window=0, scale=None, row_bl
     return res
 
 
-def forward(q, k, v, causal=True, window=0, scale=None, row_block=256, sink=0):
+def forward(q, k, v, causal=True, window=0, scale=None, row_block=256, sink=0, cu_seqlens=None):
     """Returns (O, LSE) in float64."""
-    r = forward_backward(q, k, v, None, causal, window, scale, row_block, sink)
+    r = forward_backward(q, k, v, None, causal, window, scale, row_block, sink, cu_seqlens)
     return r["O"], r["LSE"]
 
 
-def backward(q, k, v, do, causal=True, window=0, scale=None, row_block=256, sink=0):
+def backward(q, k, v, do, causal=True, window=0, scale=None, row_block=256, sink=0, cu_seqlens=None):
     """Returns (dQ, dK, dV) in float64: the exact gradient of sum(O * dO)."""
-    r = forward_backward(q, k, v, do, causal, window, scale, row_block, sink)
+    r = forward_backward(q, k, v, do, causal, window, scale, row_block, sink, cu_seqlens)
     return r["dQ"], r["dK"], r["dV"]
 
 
@@ -187,27 +207,30 @@ def probabilities(q, k, b, h, causal=True, window=0, scale=None, sink=0):
     return head_rows(qh, kh, kh, np.arange(S), causal, window, scale, None, k.shape[2] - S, sink)["P"]
 
 
-def rows_forward(q, k, v, b, h, rows, causal=True, window=0, scale=None, sink=0):
+def rows_forward(q, k, v, b, h, rows, causal=True, window=0, scale=None, sink=0, cu_seqlens=None):
     """O[b, h, rows] and LSE[b, h, rows], each row computed on its own."""
     B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     g = kv_head(h, Hq, Hkv)
     qh, kh, vh = _f64(q[b, h], k[b, g], v[b, g])
-    t = head_rows(qh, kh, vh, rows, causal, window, scale, None, Sk - S, sink)
+    t = head_rows(qh, kh, vh, rows, causal, window, scale, None, Sk - S, sink,
+                  None if cu_seqlens is None else cu_seqlens[b])
     return t["O"], t["LSE"]
 
 
-def rows_dq(q, k, v, do, b, h, rows, causal=True, window=0, scale=None, sink=0):
+def rows_dq(q, k, v, do, b, h, rows, causal=True, window=0, scale=None, sink=0, cu_seqlens=None):
     """dQ[b, h, rows]: each row needs only its own probabilities and dP row."""
     B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     g = kv_head(h, Hq, Hkv)
     qh, kh, vh, doh = _f64(q[b, h], k[b, g], v[b, g], do[b, h])
-    t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S, sink)
+    t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S, sink,
+                  None if cu_seqlens is None else cu_seqlens[b])
     return scale * (t["dS"] @ kh)
 
 
-def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_block=256, sink=0):
+def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_block=256, sink=0,
+              cu_seqlens=None):
     """dK[b, g, cols] and dV[b, g, cols]: sums over every query head of group g and every
     query row that can see at least one of `cols`."""
     B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
@@ -215,7 +238,8 @@ def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_bl
     cols = np.asarray(cols, dtype=np.int64)
     G = Hq // Hkv
     kh, vh = _f64(k[b, g], v[b, g])
-    need = visible_mask(np.arange(S), cols, causal, window, Sk - S, sink).any(axis=1)
+    docs = None if cu_seqlens is None else cu_seqlens[b]
+    need = visible_mask(np.arange(S), cols, causal, window, Sk - S, sink, docs).any(axis=1)
     rows_all = np.nonzero(need)[0]
     dK = np.zeros((cols.size, D))
     dV = np.zeros((cols.size, D))
@@ -223,7 +247,7 @@ def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_bl
         qh, doh = _f64(q[b, h], do[b, h])
         for r0 in range(0, rows_all.size, row_block):
             rows = rows_all[r0:r0 + row_block]
-            t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S, sink)
+            t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S, sink, docs)
             dK += scale * (t["dS"][:, cols].T @ qh[rows])
             dV += t["P"][:, cols].T @ doh[rows]
     return dK, dV

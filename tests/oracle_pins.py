@@ -19,7 +19,10 @@ a transposed operand, an off-by-one mask -- fails at least one of them):
     counts are the size of the union of the window and the sink range;
   * paged caches: an identity block layout reproduces the dense result exactly, shuffling the
     physical blocks (with the table) changes no bit, sequences of different lengths equal their
-    own dense problems, and blocks shared by two sequences serve both.
+    own dense problems, and blocks shared by two sequences serve both;
+  * packed documents: the packed result equals each document run as its own sequence (all five
+    tensors), one document equals plain attention, one-token documents give O = V, and zero-query
+    counts restart at every boundary.
 """
 from __future__ import annotations
 
@@ -108,7 +111,7 @@ def pin_fd_sampled(A, seed=1, n_entries=256, n_dirs=16, tol=1e-6):
 
 
 # ---------------------------------------------------------------- scalar brute force
-def _brute(q, k, v, do, causal, window, scale, sink=0):
+def _brute(q, k, v, do, causal, window, scale, sink=0, cu=None):
     """Pure-Python loops; softmax derivative through the full Jacobian dP_k/dx_j = P_k (d_kj - P_j).
     With Sq queries and Sk keys, query i stands at position i + Sk - Sq."""
     B, Hq, S, D = q.shape
@@ -126,6 +129,9 @@ def _brute(q, k, v, do, causal, window, scale, sink=0):
                 pos = i + Sk - S
                 vis = [j for j in range(Sk)
                        if (not causal or j <= pos) and (window == 0 or pos - j < window or j < sink)]
+                if cu is not None:  # same document: the last boundary at or before each position
+                    doc = lambda t: max(c for c in range(len(cu[b]) - 1) if cu[b][c] <= t)  # noqa: E731
+                    vis = [j for j in vis if doc(j) == doc(pos)]
                 x = {j: scale * sum(q[b, h, i, d] * k[b, g, j, d] for d in range(D)) for j in vis}
                 mx = max(x.values())
                 z = sum(math.exp(x[j] - mx) for j in vis)
@@ -588,6 +594,72 @@ def pin_paged_lengths_and_sharing(A):
     assert np.array_equal(O2[0], O[0]) and not np.array_equal(O2[1], O[1])
 
 
+# ---------------------------------------------------------------- packed documents
+def pin_docs_equal_separate_sequences(A):
+    """Documents packed into one buffer behave exactly as if each were its own sequence: O, LSE
+    and dQ of a document's rows and dK, dV of its keys equal the result of running the document
+    alone (rows of other documents contribute nothing)."""
+    q, k, v, do = _rng_inputs(43, 2, 4, 2, 40, 8)
+    cu = np.array([[0, 7, 7, 25, 40], [0, 1, 2, 33, 40]])
+    for window in (0, 5):
+        r = A.forward_backward(q, k, v, do, True, window, 0.5, cu_seqlens=cu)
+        for b in range(2):
+            for d0, d1 in zip(cu[b][:-1], cu[b][1:]):
+                if d1 == d0:
+                    continue
+                sl = slice(d0, d1)
+                sub = A.forward_backward(q[b:b + 1, :, sl], k[b:b + 1, :, sl], v[b:b + 1, :, sl],
+                                         do[b:b + 1, :, sl], True, window, 0.5)
+                for name in ("O", "LSE", "dQ", "dK", "dV"):
+                    got = r[name][b, :, sl]
+                    assert np.max(np.abs(got - sub[name][0])) <= 1e-13, (b, d0, d1, window, name)
+
+
+def pin_docs_special_cases(A):
+    """One document is plain attention; one-token documents make every query see only its own
+    key: O = V (group-repeated), LSE = s <q_i, k_i>, dQ = dK = 0, dV = group sum of dO."""
+    q, k, v, do = _rng_inputs(44, 1, 4, 2, 12, 8)
+    plain = A.forward_backward(q, k, v, do, True, 0, 0.5)
+    one = A.forward_backward(q, k, v, do, True, 0, 0.5, cu_seqlens=np.array([[0, 12]]))
+    for name in ("O", "LSE", "dQ", "dK", "dV"):
+        assert np.array_equal(plain[name], one[name]), name
+    r = A.forward_backward(q, k, v, do, True, 0, 0.5, cu_seqlens=np.arange(13)[None])
+    for h in range(4):
+        g = h // 2
+        assert np.max(np.abs(r["O"][0, h] - v[0, g])) <= 1e-14
+        assert np.max(np.abs(r["LSE"][0, h] - 0.5 * np.sum(q[0, h] * k[0, g], axis=1))) <= 1e-13
+    assert np.max(np.abs(r["dQ"])) <= 1e-14 and np.max(np.abs(r["dK"])) <= 1e-14
+    assert np.max(np.abs(r["dV"] - do.reshape(1, 2, 2, 12, 8).sum(axis=2))) <= 1e-13
+
+
+def pin_docs_zero_query_counts(A):
+    """Q = 0: exp(LSE) counts the keys from the document start (or the window start, if later)
+    up to the query."""
+    S = 60
+    q, k, v, _ = _rng_inputs(45, 1, 2, 1, S, 4)
+    q[:] = 0.0
+    cu = np.array([[0, 5, 6, 30, 31, 60]])
+    for W in (0, 1, 4, 20):
+        _, LSE = A.forward(q, k, v, True, W, 1.0, cu_seqlens=cu)
+        p = np.arange(S)
+        start = np.array([max(c for c in cu[0][:-1] if c <= t) for t in p])
+        if W:
+            start = np.maximum(start, p - W + 1)
+        assert np.array_equal(np.rint(np.exp(LSE[0, 0])).astype(np.int64), p - start + 1), W
+
+
+def pin_docs_bruteforce(A, tol=1e-12):
+    for (Hq, Hkv, S, D, window, cu, seed) in ((2, 1, 9, 3, 0, [[0, 4, 9]], 46), (4, 2, 10, 2, 3, [[0, 1, 5, 5, 10]], 47)):
+        q, k, v, do = _rng_inputs(seed, 1, Hq, Hkv, S, D)
+        cu = np.asarray(cu)
+        r = A.forward_backward(q, k, v, do, True, window, 0.7, cu_seqlens=cu)
+        ref = _brute(q, k, v, do, True, window, 0.7, 0, cu)
+        for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"),
+                              (r["O"], r["LSE"], r["dQ"], r["dK"], r["dV"]), ref):
+            err = np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30)
+            assert err <= tol, f"docs brute force {name}: {err:.3e}"
+
+
 ALL_PINS = [
     pin_fd_every_entry, pin_bruteforce, pin_torch_sdpa, pin_three_token_closed_form,
     pin_constant_v, pin_identical_keys, pin_window_one, pin_zero_queries, pin_rows_sum_to_one,
@@ -596,4 +668,6 @@ ALL_PINS = [
     pin_single_decode_query, pin_chunk_helpers, pin_sink_decode_is_concatenation,
     pin_sinks_covering_all_keys, pin_sink_zero_query_counts, pin_sink_chunk_is_suffix_of_square,
     pin_sink_helpers, pin_paged_matches_dense, pin_paged_lengths_and_sharing,
+    pin_docs_equal_separate_sequences, pin_docs_special_cases, pin_docs_zero_query_counts,
+    pin_docs_bruteforce,
 ]

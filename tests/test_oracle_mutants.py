@@ -16,8 +16,8 @@ _real_gather = PG.gather_sequence
 
 
 def _head_rows_mut(kind):
-    def f(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0, sink=0):
-        t = _real_head_rows(qh, kh, vh, rows, causal, window, scale, doh, offset, sink)
+    def f(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0, sink=0, docs=None):
+        t = _real_head_rows(qh, kh, vh, rows, causal, window, scale, doh, offset, sink, docs)
         if doh is not None:
             if kind == "dropped_delta":          # dS = P * dP (rowsum term dropped)
                 t["dS"] = t["P"] * t["dP"]
@@ -34,8 +34,8 @@ def _head_rows_mut(kind):
 
 
 def _fb_mut(kind):
-    def f(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256, sink=0):
-        r = _real_fb(q, k, v, do, causal, window, scale, row_block, sink)
+    def f(q, k, v, do=None, causal=True, window=0, scale=None, row_block=256, sink=0, cu_seqlens=None):
+        r = _real_fb(q, k, v, do, causal, window, scale, row_block, sink, cu_seqlens)
         s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
         if kind == "lse_base2":
             r["LSE"] = r["LSE"] / math.log(2.0)
@@ -49,7 +49,7 @@ def _fb_mut(kind):
 
 
 def _mask_mut(kind):
-    def f(rows, cols, causal, window, offset=0, sink=0):
+    def f(rows, cols, causal, window, offset=0, sink=0, docs=None):
         if kind == "offset_ignored":          # queries aligned top-left instead of bottom-right
             offset = 0
         elif kind == "offset_negated":
@@ -71,6 +71,12 @@ def _mask_mut(kind):
             else:
                 sk = inw | (j < sink)
             m &= sk
+        if docs is not None and kind != "docs_ignored":
+            di, dj = A.document_of(i, docs), A.document_of(j, docs)
+            if kind == "doc_leaks_previous":      # a query also sees the document before its own
+                m &= (di == dj) | (di == dj + 1)
+            else:
+                m &= di == dj
         return m
     return f
 
@@ -105,6 +111,8 @@ MUTANTS = {
     "sink_ignored": ("visible_mask", _mask_mut("sink_ignored")),
     "sink_off_by_one": ("visible_mask", _mask_mut("sink_off_by_one")),
     "sink_without_causal": ("visible_mask", _mask_mut("sink_without_causal")),
+    "doc_leaks_previous": ("visible_mask", _mask_mut("doc_leaks_previous")),
+    "docs_ignored": ("visible_mask", _mask_mut("docs_ignored")),
     "paged_slot_reversed": ("paged.gather_sequence", _gather_mut("paged_slot_reversed")),
     "paged_table_of_sequence_0": ("paged.gather_sequence", _gather_mut("paged_table_of_sequence_0")),
 }
