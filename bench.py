@@ -136,11 +136,18 @@ def cpu_baseline(w, q, k, v, do, heads: int):
     G = w.Hq // w.Hkv
     heads = max(G, min(w.Hq, heads // G * G))
     groups = heads // G
+    cu = None
+    pairs = attended_pairs(w.S, w.causal, w.window, w.n_q, w.sink)
+    if w.docs:
+        from causal_attention_fa2_amd.workloads import document_boundaries
+        cu = document_boundaries(w)
+        pairs = sum(attended_pairs(int(b - a), True, w.window) for row in cu
+                    for a, b in zip(row[:-1], row[1:]) if b > a) / w.B
     t0 = time.perf_counter()
     oracle.forward_backward(q[:, :heads], k[:, :groups], v[:, :groups], do[:, :heads],
-                            w.causal, w.window, w.scale, sink=w.sink)
+                            w.causal, w.window, w.scale, sink=w.sink, cu_seqlens=cu)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.B * heads * attended_pairs(w.S, w.causal, w.window, w.n_q, w.sink) * w.D * 3.5
+    flops = 4.0 * w.B * heads * pairs * w.D * 3.5
     model, blas = host_info()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle fwd+bwd on {heads} of {w.Hq} query heads ({groups} KV groups), "
@@ -259,17 +266,27 @@ def main() -> int:
     dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
     ws_bytes = fa.attn_bwd_qk_workspace_bytes(w.B, w.Hq, w.Hkv, Sq, w.S, w.D)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    # the square workloads go through attn_fwd / attn_bwd, the others through the _qk entry points
+    # the square workloads go through attn_fwd / attn_bwd, packed documents through the _varlen
+    # entry points, the others through the _qk entry points
     square = Sq == w.S and not w.sink
+    cu = None
+    if w.docs:
+        from causal_attention_fa2_amd.workloads import document_boundaries
+        cu = document_boundaries(w)
+        tcu = torch.from_numpy(cu).cuda()
 
     def fwd():
-        if square:
+        if cu is not None:
+            fa.attn_fwd_varlen(tq, tk, tv, o, lse, tcu, w.window, w.scale)
+        elif square:
             fa.attn_fwd(tq, tk, tv, o, lse, w.causal, w.window, w.scale)
         else:
             fa.attn_fwd_qk(tq, tk, tv, o, lse, w.causal, w.window, w.scale, None, w.sink)
 
     def bwd():
-        if square:
+        if cu is not None:
+            fa.attn_bwd_varlen(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, tcu, w.window, w.scale)
+        elif square:
             fa.attn_bwd(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window, w.scale)
         else:
             fa.attn_bwd_qk(tq, tk, tv, o, lse, tdo, dq, dk, dv, ws, w.causal, w.window, w.scale, None,
@@ -329,7 +346,11 @@ def main() -> int:
         d = [evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2)]
         kern_ms[name] = sum(d) / len(d)
 
-    N = attended_pairs(w.S, w.causal, w.window, Sq, w.sink)
+    if cu is not None:  # per batch row and document, the same convention per document
+        N = sum(attended_pairs(int(b - a), True, w.window) for row in cu for a, b in zip(row[:-1], row[1:])
+                if b > a) / w.B
+    else:
+        N = attended_pairs(w.S, w.causal, w.window, Sq, w.sink)
     unit = 2.0 * w.B * w.Hq * N * w.D  # one GEMM-sized pass over the attended pairs
     fl = {"attn_fwd": 2 * unit, "attn_bwd_dkdv": 4 * unit, "attn_bwd_dq": 1 * unit}
     total_flops = 7 * unit  # forward (2) + backward counted as 2.5x forward (5)
@@ -369,7 +390,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
                    "causal": w.causal, "window": w.window, "parallelism": "none (1 GPU)",
-                   **({"Sq": Sq} if Sq != w.S else {}), **({"sink": w.sink} if w.sink else {})},
+                   **({"Sq": Sq} if Sq != w.S else {}), **({"sink": w.sink} if w.sink else {}),
+                   **({"documents": [int(x) for x in cu[0]]} if cu is not None else {})},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "phase_ms": phases,
         "phase_tflops_median": {

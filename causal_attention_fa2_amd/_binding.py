@@ -56,6 +56,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i,
                                    f, vp]
     lib.attn_fwd_paged.restype = i
+    lib.attn_fwd_varlen.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_varlen.restype = i
+    lib.attn_bwd_varlen.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, i,
+                                    i, i, i, i, i, i, f, vp]
+    lib.attn_bwd_varlen.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -192,6 +197,41 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlen_k, o, lse, causal: boo
         block_table.shape[1], nb, int(bool(causal)), int(window), int(sink), scale, _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_paged")
+
+
+def _docs_arg(cu_seqlens, B, device):
+    import torch
+    if cu_seqlens.dim() != 2 or cu_seqlens.shape[0] != B or cu_seqlens.shape[1] < 2:
+        raise ValueError("cu_seqlens must be [B, n_docs + 1]")
+    _check_tensor("cu_seqlens", cu_seqlens, tuple(cu_seqlens.shape), torch.int32, device)
+    return cu_seqlens.data_ptr(), cu_seqlens.shape[1] - 1
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, window: int = 0, scale: float | None = None,
+                    stream=None) -> None:
+    """Calls attn_fwd_varlen (causal, packed documents): cu_seqlens int32 [B, n_docs + 1]."""
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), (_, w, sc) = _fwd_args(q, k, v, o, lse, True, window, scale)
+    if Sq != Sk:
+        raise ValueError("packed documents take as many queries as keys")
+    cu, n = _docs_arg(cu_seqlens, B, q.device)
+    st = load_library().attn_fwd_varlen(_dtype_code(q), *ptrs, cu, n, B, Hq, Hkv, Sq, D, w, sc,
+                                        _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_varlen")
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, window: int = 0,
+                    scale: float | None = None, stream=None) -> None:
+    """Calls attn_bwd_varlen; workspace as for attn_bwd (attn_bwd_workspace_bytes)."""
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), (_, w, sc) = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv,
+                                                          workspace, True, window, scale)
+    if Sq != Sk:
+        raise ValueError("packed documents take as many queries as keys")
+    cu, n = _docs_arg(cu_seqlens, B, q.device)
+    st = load_library().attn_bwd_varlen(_dtype_code(q), *ptrs, cu, n, B, Hq, Hkv, Sq, D, w, sc,
+                                        _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_varlen")
 
 
 def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale):

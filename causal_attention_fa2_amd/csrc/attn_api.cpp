@@ -9,7 +9,9 @@
 // (same section: one kernel for prefill and for one-token decode against a cache), and more
 // queries than keys is not defined; sink keys ("KYNETRA FOUNDRY", Vaultecho paragraph) are a count
 // >= 0 of leading keys that stay visible beside the window; a paged cache ("KYNETRA FOUNDRY",
-// paged-KV paragraph) uses power-of-two blocks of at least 16 tokens.
+// paged-KV paragraph) uses power-of-two blocks of at least 16 tokens; packed documents (page
+// "Build a standalone, production grade system that trains a 4,...", curriculum section) take
+// the causal mask, no sinks and at most kMaxDocs documents per batch row.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -182,6 +184,77 @@ int attn_fwd_paged(int dtype, const void* q, const void* k_pool, const void* v_p
   a.pg.max_blocks = max_blocks;
   a.pg.num_blocks = num_blocks;
   return fa::launch_fwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int n_docs, int B, int Hq, int Hkv, int S, int D,
+                    int window, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return ATTN_ERR_INVALID;
+  if (n_docs <= 0) return ATTN_ERR_INVALID;
+  if (n_docs > fa::kMaxDocs) return ATTN_ERR_UNSUPPORTED;
+  int st = check_common(dtype, B, Hq, Hkv, S, S, D, 1, window, 0, scale);
+  if (st != ATTN_OK) return st;
+  fa::Args a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = S;
+  a.Sk = S;
+  a.D = D;
+  a.causal = 1;
+  a.window = window;
+  a.scale = scale;
+  a.stream = stream;
+  a.docs.cu = cu_seqlens;
+  a.docs.n = n_docs;
+  return fa::launch_fwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+int attn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, const int* cu_seqlens, int n_docs,
+                    int B, int Hq, int Hkv, int S, int D, int window, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace || !cu_seqlens)
+    return ATTN_ERR_INVALID;
+  if (n_docs <= 0) return ATTN_ERR_INVALID;
+  if (n_docs > fa::kMaxDocs) return ATTN_ERR_UNSUPPORTED;
+  int st = check_common(dtype, B, Hq, Hkv, S, S, D, 1, window, 0, scale);
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, Hkv, S, S, D)) return ATTN_ERR_INVALID;
+  fa::Args a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o_in = o;
+  a.lse = const_cast<float*>(lse);
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const size_t row_bytes = fa::delta_bytes(B, Hq, S);
+  a.delta = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + row_bytes);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_bytes);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = S;
+  a.Sk = S;
+  a.D = D;
+  a.causal = 1;
+  a.window = window;
+  a.scale = scale;
+  a.stream = stream;
+  a.docs.cu = cu_seqlens;
+  a.docs.n = n_docs;
+  return fa::launch_bwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
 const char* attn_status_string(int status) {

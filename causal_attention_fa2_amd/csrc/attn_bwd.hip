@@ -61,14 +61,13 @@ __global__ __launch_bounds__(256) void delta_kernel(const typename E::T* __restr
   }
 }
 
-template <class E, int D, int NW, int KB>
+template <class E, int D, int NW, int KB, bool VL>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dQ,
     int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale,
-    float scale_log2,
-    int n_qt) {
+    float scale_log2, int n_qt, Docs docs) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 32 * KB;
   constexpr int DS = D / 16;
@@ -79,6 +78,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
   __shared__ __attribute__((aligned(1024))) char st2[kStage];
+  __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
 
   const int lane = lane_id();
   const int w = wave_id();
@@ -107,10 +107,19 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   const int pw = qw + off;  // positions of this wave's rows
   const int my_p = my_q + off;
 
+  // documents: ds_lane = start of this lane's query's document
+  int ds_lane = 0;
+  if constexpr (VL) {
+    stage_docs(cu_s, docs.cu + (size_t)b * (docs.n + 1), docs.n, S);
+    __syncthreads();
+    ds_lane = doc_start(cu_s, docs.n, imin_(my_p, S - 1));
+  }
+
   // key tiles: the sink tiles [0, jt_ns) then the window tiles [jt_lo, jt_hi]
   int jt_ns, jt_lo, jt_hi;
   kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, sink, &jt_ns, &jt_lo,
                 &jt_hi);
+  if constexpr (VL) jt_lo = imax_(jt_lo, doc_start(cu_s, docs.n, q0 + off) / BC);  // no sinks here
   const int n_steps = jt_ns + jt_hi - jt_lo + 1;
   auto tile_of = [&](int s) __attribute__((always_inline)) { return s < jt_ns ? s : jt_lo + s - jt_ns; };
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
@@ -139,7 +148,11 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const char* v_lds = k_lds + KvTile::kBytes;
     const int j0 = tile_of(s) * BC;
     if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink)) return;
-    const bool full = block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink);
+    bool full = block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink);
+    if constexpr (VL) {
+      if (j0 + BC - 1 < __builtin_amdgcn_readlane(ds_lane, 0)) return;
+      full = full && __builtin_amdgcn_readlane(ds_lane, 31) <= j0;
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16_t st = f32x16_t{}, dpt = f32x16_t{};
@@ -149,11 +162,14 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
         mma(dpt, RowFrag<E, KvTile>::get(v_lds, 32 * kb + l32, s2), df[s2]);
       }
       auto grad = [&](auto maskc) __attribute__((always_inline)) {
+        int mp = 0;  // this lane's position, re-derived inside the masked path only
+        if constexpr (decltype(maskc)::value) mp = opaque(my_p);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = __builtin_amdgcn_exp2f(fmaf(st[r], scale_log2, nlse2));
           if constexpr (decltype(maskc)::value) {
-            if (!visible(my_p, j0 + 32 * kb + acc_row(r), S, causal, window, sink)) p = 0.f;
+            const int j = j0 + 32 * kb + acc_row(r);
+            if (!visible(mp, j, S, causal, window, sink) || (VL && j < ds_lane)) p = 0.f;
           }
           st[r] = p * (dpt[r] - dl);
         }
@@ -224,11 +240,11 @@ static int launch_bwd_t(const Args& a) {
     const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
     dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
     notify_launch("attn_bwd_dq", 0, a.stream);
-    hipLaunchKernelGGL((dq_kernel<E, D, NW, KB>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
-                       (T*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, a.scale,
-                       scale_log2,
-                       n_qt);
+    auto kern = a.docs.cu ? dq_kernel<E, D, NW, KB, true> : dq_kernel<E, D, NW, KB, false>;
+    hipLaunchKernelGGL(kern, grid, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                       (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta, (T*)a.dq, a.B,
+                       a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt,
+                       a.docs);
     notify_launch("attn_bwd_dq", 1, a.stream);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -11,14 +11,14 @@
 
 namespace fa {
 
-template <class E, int D, int NW, int QB>
+template <class E, int D, int NW, int QB, bool VL>
 __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dK,
     typename E::T* __restrict__ dV, float* __restrict__ part, int B, int Hq, int Hkv, int Sq,
     int S, int causal, int window, int sink, float scale, float scale_log2, int n_kt, int n_pairs,
-    int hs) {
+    int hs, Docs docs) {
   constexpr int BC = 32 * NW;  // keys per workgroup
   constexpr int BR = 32 * QB;  // query rows per streamed tile
   constexpr int DS = D / 16;
@@ -31,6 +31,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
   __shared__ __attribute__((aligned(1024))) char st2[kStage];
+  __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
 
   const int lane = lane_id();
   const int w = wave_id();
@@ -54,6 +55,11 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   const bool two = tb > ta;
   const size_t kv_off = (size_t)bg * S * D;
   const int qoff = S - Sq;  // query row r stands at key position r + qoff
+  if constexpr (VL) {
+    stage_docs(cu_s, docs.cu + (size_t)b * (docs.n + 1), docs.n, S);
+    __syncthreads();
+  }
+  int de_lane = 0;  // documents: end of this lane's key's document (rows at or past it cannot see it)
 
   // Segment = one key tile: the workgroup runs key tile ta, then key tile tb.
   int kt = ta, lo = 0, nq = 0, n_steps = 0;
@@ -61,6 +67,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     int hi;
     kt = t;
     q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, sink, &lo, &hi);
+    if constexpr (VL) hi = imin_(hi, (doc_end(cu_s, docs.n, imin_(t * BC + BC - 1, S - 1)) - 1 - qoff) / BR);
     nq = imax_(hi - lo + 1, 0);  // 0: no query sees these keys, so dK = dV = 0
     n_steps = hpg * nq;
   };
@@ -88,6 +95,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   auto load_kv = [&]() __attribute__((always_inline)) {
     const int my_k = kt * BC + 32 * w + l32;
     const bool ok = my_k < S;
+    if constexpr (VL) de_lane = doc_end(cu_s, docs.n, imin_(my_k, S - 1));
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       kf[s] = load_frag_global(K + kv_off + (size_t)my_k * D + 16 * s + 8 * half, ok);
@@ -136,7 +144,12 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
     for (int qb = 0; qb < QB; ++qb) {
       const int r0 = p0 + 32 * qb;
       if (block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window, sink)) continue;
-      const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
+      bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
+      if constexpr (VL) {
+        // every row at or past the last key's document end: empty; all before the first key's: full
+        if (r0 >= __builtin_amdgcn_readlane(de_lane, 31)) continue;
+        full = full && r0 + 31 < __builtin_amdgcn_readlane(de_lane, 0);
+      }
       // All Q / dO row fragments of this block in flight before the S / dP products, so the
       // LDS latency is paid once per block rather than once per MFMA.
       Frag<E> qa[DS], da[DS];
@@ -171,7 +184,8 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
             const int r = 4 * r4 + c;
             float p = __builtin_amdgcn_exp2f(fmaf(sa[r], scale_log2, -lse4[c]));
             if constexpr (decltype(maskc)::value) {
-              if (!visible(p0 + rb + c, my_k, S, causal, window, sink)) p = 0.f;
+              const int i = p0 + rb + c;
+              if (!visible(i, my_k, S, causal, window, sink) || (VL && i >= de_lane)) p = 0.f;
             }
             sa[r] = p;
             dp[r] = p * (dp[r] - dl4[c]);
@@ -267,14 +281,13 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
 // vector work (exponentials, dS) can run while its partner issues matrix products on the shared
 // SIMD. Per wave: its K or V fragments (B operand), its dV or dK accumulators and the two blocks'
 // S / dP accumulators -- the two roles' state shares the same registers.
-template <int D, int QB>
+template <int D, int QB, bool VL>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part, int B, int Hq,
     int Hkv, int Sq, int S, int causal, int window, int sink, float scale, float scale_log2,
-    int n_kt,
-    int n_pairs, int hs) {
+    int n_kt, int n_pairs, int hs, Docs docs) {
   typedef BF16 E;
   constexpr int NW = 8;        // waves
   constexpr int NP = 4;        // wave pairs, 32 keys each
@@ -291,6 +304,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
   __shared__ __attribute__((aligned(1024))) char st2[kStage];
   __shared__ __attribute__((aligned(1024))) char pbuf[NP * QB * kPBlock];
+  __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
 
   const int lane = lane_id();
   const int w = wave_id();
@@ -316,12 +330,18 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   const bool two = tb > ta;
   const size_t kv_off = (size_t)bg * S * D;
   const int qoff = S - Sq;  // query row r stands at key position r + qoff
+  if constexpr (VL) {
+    stage_docs(cu_s, docs.cu + (size_t)b * (docs.n + 1), docs.n, S);
+    __syncthreads();
+  }
+  int de_lane = 0;  // documents: end of this lane's key's document (rows at or past it cannot see it)
 
   int kt = ta, lo = 0, nq = 0, n_steps = 0;
   auto set_segment = [&](int t) __attribute__((always_inline)) {
     int hi;
     kt = t;
     q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, sink, &lo, &hi);
+    if constexpr (VL) hi = imin_(hi, (doc_end(cu_s, docs.n, imin_(t * BC + BC - 1, S - 1)) - 1 - qoff) / BR);
     nq = imax_(hi - lo + 1, 0);  // 0: no query sees these keys, so dK = dV = 0
     n_steps = hpg * nq;
   };
@@ -346,6 +366,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   auto load_kv = [&]() __attribute__((always_inline)) {
     const int my_k = kt * BC + 32 * pw + l32;
     const bool ok = my_k < S;
+    if constexpr (VL) de_lane = doc_end(cu_s, docs.n, imin_(my_k, S - 1));
     const uint16_t* src = (srole ? K : V) + kv_off + (size_t)my_k * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < DS; ++s) kvf[s] = load_frag_global(src + 16 * s, ok);
@@ -387,6 +408,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     for (int qb = 0; qb < QB; ++qb) {
       const int r0 = p0 + 32 * qb;
       act[qb] = !block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
+      if constexpr (VL) act[qb] = act[qb] && r0 < __builtin_amdgcn_readlane(de_lane, 31);
       if (!act[qb]) continue;
       const char* src = srole ? q_lds : do_lds;
       Frag<E> fr[DS];
@@ -397,7 +419,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
 #pragma unroll
       for (int s2 = 0; s2 < DS; ++s2) mma(xs[qb], fr[s2], kvf[s2]);
       if (srole) {
-        const bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
+        bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
+        if constexpr (VL) full = full && r0 + 31 < __builtin_amdgcn_readlane(de_lane, 0);
         auto softmax = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
@@ -408,7 +431,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
               const int r = 4 * r4 + c;
               float p = __builtin_amdgcn_exp2f(fmaf(xs[qb][r], scale_log2, -lse4[c]));
               if constexpr (decltype(maskc)::value) {
-                if (!visible(p0 + rb + c, my_k, S, causal, window, sink)) p = 0.f;
+                const int i = p0 + rb + c;
+                if (!visible(i, my_k, S, causal, window, sink) || (VL && i >= de_lane)) p = 0.f;
               }
               xs[qb][r] = p;
             }
@@ -533,15 +557,17 @@ static int launch_dkdv_t(const Args& a) {
     dim3 grid((unsigned)(p.n_pairs * a.B * a.Hkv * p.hs));
     notify_launch("attn_bwd_dkdv", 0, a.stream);
     if constexpr (E::kBytes == 2) {
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, QB>), grid, dim3(512), 0, st, (const T*)a.q,
-                         (const T*)a.k, (const T*)a.v, (const T*)a.dout, (const float*)a.lse2,
-                         (const float*)a.delta, (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq,
-                         a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
+      auto kern = a.docs.cu ? dkdv_pair_kernel<D, QB, true> : dkdv_pair_kernel<D, QB, false>;
+      hipLaunchKernelGGL(kern, grid, dim3(512), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                         (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta, (T*)a.dk,
+                         (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink,
+                         a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs, a.docs);
     } else {
-      hipLaunchKernelGGL((dkdv_kernel<E, D, NW, QB>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
-                         (const T*)a.k, (const T*)a.v, (const T*)a.dout, (const float*)a.lse2,
-                         (const float*)a.delta, (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq,
-                         a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs);
+      auto kern = a.docs.cu ? dkdv_kernel<E, D, NW, QB, true> : dkdv_kernel<E, D, NW, QB, false>;
+      hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, st, (const T*)a.q, (const T*)a.k,
+                         (const T*)a.v, (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta,
+                         (T*)a.dk, (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window,
+                         a.sink, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs, a.docs);
     }
     notify_launch("attn_bwd_dkdv", 1, a.stream);
     if (p.hs > 1) {

@@ -29,12 +29,13 @@ namespace fa {
 // PG: K and V are pools of a paged cache read through pg (page "KYNETRA FOUNDRY", paged-KV
 // paragraph: a per-sequence block table maps token positions to pool blocks); S is then the
 // sequence's own key count.
-template <class E, int D, int NW, int KB, int NST, bool PG>
+// VL: packed documents (docs); a query sees only keys from its own document's start on.
+template <class E, int D, int NW, int KB, int NST, bool PG, bool VL>
 __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
     int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale_log2,
-    int n_qt, PagedKV pg) {
+    int n_qt, PagedKV pg, Docs docs) {
   constexpr int BR = 32 * NW;
   constexpr int BC = 32 * KB;
   constexpr int DS = D / 16;  // 16-wide contraction steps over the head dimension
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   constexpr int kOps = 2 * dma_tile_ops<E, BC, D, NW>();  // DMA instructions per wave per stage
   static_assert(NST == 2 || NST == 3, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[NST * kStage];
+  __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
 
   const int lane = lane_id();
   const int w = wave_id();
@@ -74,10 +76,19 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   const int pw = qw + off;     // positions of this wave's rows: pw .. pw + 31
   const int my_p = my_q + off;
 
+  // documents: ds_lane = start of this lane's query's document
+  int ds_lane = 0;
+  if constexpr (VL) {
+    stage_docs(cu_s, docs.cu + (size_t)b * (docs.n + 1), docs.n, S);
+    __syncthreads();
+    ds_lane = doc_start(cu_s, docs.n, imin_(my_p, S - 1));
+  }
+
   // key tiles: the sink tiles [0, jt_ns) then the window tiles [jt_lo, jt_hi]
   int jt_ns, jt_lo, jt_hi;
   kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, sink, &jt_ns, &jt_lo,
                 &jt_hi);
+  if constexpr (VL) jt_lo = imax_(jt_lo, doc_start(cu_s, docs.n, q0 + off) / BC);  // no sinks here
   const int n_steps = jt_ns + jt_hi - jt_lo + 1;
   auto tile_of = [&](int s) __attribute__((always_inline)) { return s < jt_ns ? s : jt_lo + s - jt_ns; };
 
@@ -140,8 +151,8 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          if (!visible(my_p, j0 + 32 * kb + acc_row(r), S, causal, window, sink))
-            st[kb][r] = kNegInf;
+          const int j = j0 + 32 * kb + acc_row(r);
+          if (!visible(my_p, j, S, causal, window, sink) || (VL && j < ds_lane)) st[kb][r] = kNegInf;
           mx = fmaxf(mx, st[kb][r]);
         }
       }
@@ -195,7 +206,13 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
     const int j0 = tile_of(s) * BC;
     if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink)) return;
-    compute_general(j0, k_lds, block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink));
+    bool full = block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink);
+    if constexpr (VL) {
+      // every key before the first row's document start: empty; all after the last row's: full
+      if (j0 + BC - 1 < __builtin_amdgcn_readlane(ds_lane, 0)) return;
+      full = full && __builtin_amdgcn_readlane(ds_lane, 31) <= j0;
+    }
+    compute_general(j0, k_lds, full);
   };
 
   ring_run<NST, kStage, kOps>(ring, n_steps, issue, compute);
@@ -229,10 +246,13 @@ static int launch_fwd_t(const Args& a) {
   dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   notify_launch("attn_fwd", 0, a.stream);
-  auto kern = a.paged ? fwd_kernel<E, D, NW, KB, NST, true> : fwd_kernel<E, D, NW, KB, NST, false>;
+  auto kern = a.paged ? fwd_kernel<E, D, NW, KB, NST, true, false>
+                       : (a.docs.cu ? fwd_kernel<E, D, NW, KB, NST, false, true>
+                                    : fwd_kernel<E, D, NW, KB, NST, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, (hipStream_t)a.stream, (const typename E::T*)a.q,
                      (const typename E::T*)a.k, (const typename E::T*)a.v, (typename E::T*)a.o, a.lse,
-                     a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, scale_log2, n_qt, a.pg);
+                     a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, scale_log2, n_qt, a.pg,
+                     a.docs);
   notify_launch("attn_fwd", 1, a.stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

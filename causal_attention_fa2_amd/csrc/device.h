@@ -435,6 +435,20 @@ __device__ __forceinline__ void ring_run(char* ring, int n, Issue&& issue, Compu
   }
 }
 
+// Returns x through an empty volatile asm statement, inside a rarely taken branch: values derived
+// from it cannot be hoisted out of the loop (where they would hold registers for the whole
+// kernel), and the branch cannot be if-converted into the common path.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Copies the document boundaries cu[0..n] of one batch row into LDS, clamped to [0, S] (the whole
+// workgroup takes part; the caller then synchronises the workgroup).
+__device__ __forceinline__ void stage_docs(int* dst, const int* __restrict__ src, int n, int S) {
+  for (int t = threadIdx.x; t <= n; t += blockDim.x) dst[t] = imin_(imax_(src[t], 0), S);
+}
+
 // Accumulator row index (within a 32 x 32 tile) held in register r by this lane.
 __device__ __forceinline__ int acc_row(int r) { return 8 * (r >> 2) + 4 * (lane_id() >> 5) + (r & 3); }
 

@@ -18,6 +18,14 @@ struct PagedKV {
   int num_blocks;
 };
 
+// Packed documents: cu [B, n + 1] int32 boundaries per batch row (device array); cu == nullptr:
+// none. At most kMaxDocs documents per row (their boundaries are staged in LDS).
+struct Docs {
+  const int* cu;
+  int n;
+};
+constexpr int kMaxDocs = 2047;
+
 struct Args {
   int dtype;
   const void* q;
@@ -39,6 +47,7 @@ struct Args {
   void* stream;
   bool paged;  // forward only: k, v are pools read through pg (Sk is then per sequence)
   PagedKV pg;
+  Docs docs;   // packed documents (Sq = Sk, causal, no sinks)
 };
 
 // Tells the launch observer (attn_set_launch_hook) that `kernel` is about to be / has been

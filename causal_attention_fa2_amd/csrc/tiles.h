@@ -88,6 +88,25 @@ ATTN_HD void q_tile_range(int c0, int c1, int S, int off, int br, bool causal, i
   *hi = imax / br;
 }
 
+// Packed documents (page "Build a standalone, production grade system that trains a 4,...",
+// curriculum section: documents concatenated into one buffer with boundary index arrays; attention
+// resets at each boundary). cu[0..n] are the boundaries, 0 = cu[0] <= ... <= cu[n] = S; position t
+// lies in document k = doc_index(cu, n, t), i.e. cu[k] <= t < cu[k + 1]. A key j is visible to a
+// query i of the same batch row only if j >= cu[k(i)] (equivalently i < cu[k(j) + 1] under the
+// causal mask), on top of the rules above. The search reads only cu[0..n] and ends after at most
+// log2(n) + 1 steps whatever the array holds.
+ATTN_HD int doc_index(const int* cu, int n, int pos) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= pos) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+ATTN_HD int doc_start(const int* cu, int n, int pos) { return cu[doc_index(cu, n, pos)]; }
+ATTN_HD int doc_end(const int* cu, int n, int pos) { return cu[doc_index(cu, n, pos) + 1]; }
+
 }  // namespace fa
 
 #endif  // ATTN_TILES_H_

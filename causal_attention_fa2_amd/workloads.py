@@ -22,6 +22,8 @@ measured and checked on; no dataset is involved, every input is synthetic):
                          one decode query each (forward only), Hq=64, Hkv=8, D=128, bf16
   paged-chunk-b4-q512-gqa64x8  4 sequences of U[2048, 8192] keys in 64-token blocks, a 512-query
                          prefill chunk each (forward only)
+  docs-gqa64x8-s8192-d128  one 8192-token buffer of packed documents of U[64, 2048] tokens
+                         (the last one cut to fit), Hq=64, Hkv=8, D=128, bf16, causal
 
 Draw order per workload: numpy.random.default_rng(seed); Q, K, V, dO as float32
 standard normals in that order (Q and dO with Sq rows, K and V with S rows) (dO then scaled by its standard deviation); then, for the
@@ -54,6 +56,7 @@ class Workload:
     sink: int = 0  # leading keys that stay visible beside the window
     paged: int = 0  # > 0: K/V in a paged pool of blocks of this many tokens (forward only)
     len_min: int = 0  # paged: sequence b holds U[len_min, S] keys
+    docs: tuple = ()  # (min, max): packed documents of U[min, max] tokens per batch row
 
     @property
     def scale(self) -> float:
@@ -85,6 +88,8 @@ WORKLOADS = {
                  paged=16, len_min=1024),
         Workload("paged-chunk-b4-q512-gqa64x8", 4, 64, 8, 8192, 128, "bf16", True, 0, 1010, Sq=512,
                  paged=64, len_min=2048),
+        Workload("docs-gqa64x8-s8192-d128", 1, 64, 8, 8192, 128, "bf16", True, 0, 1011, do_std=0.1,
+                 docs=(64, 2048)),
     )
 }
 
@@ -166,6 +171,21 @@ def paged_layout(w: Workload, k: np.ndarray, v: np.ndarray):
             kp[phys, :, :n] = k[b, :, t * bs:t * bs + n]
             vp[phys, :, :n] = v[b, :, t * bs:t * bs + n]
     return kp, vp, table, lens
+
+
+def document_boundaries(w: Workload) -> np.ndarray:
+    """cu_seqlens [B, n + 1] int32 for a packed-document workload: per batch row, documents of
+    U[docs[0], docs[1]] tokens (seeded) until S is filled, the last one cut to fit; rows with fewer
+    documents repeat S at the end."""
+    rng = np.random.default_rng(w.seed + 104729)
+    rows = []
+    for _ in range(w.B):
+        cu = [0]
+        while cu[-1] < w.S:
+            cu.append(min(w.S, cu[-1] + int(rng.integers(w.docs[0], w.docs[1] + 1))))
+        rows.append(cu)
+    n = max(len(r) for r in rows)
+    return np.array([r + [w.S] * (n - len(r)) for r in rows], dtype=np.int32)
 
 
 def random_tensor(shape, dtype: str, seed: int, std: float = 1.0) -> np.ndarray:

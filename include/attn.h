@@ -17,6 +17,9 @@
  *   tokens at the start of the sequence stay attended. Same page, paged-KV paragraph: a sequence's
  *   K/V cache lives in fixed-size blocks anywhere in a global pool, found through a per-sequence
  *   block table (attn_fwd_paged).
+ *   "Build a standalone, production grade system that trains a 4,..." (page-4 prompt), curriculum
+ *   section: documents are packed contiguously into fixed-length buffers with document-boundary
+ *   index arrays, attention being reset at each boundary (attn_fwd_varlen / attn_bwd_varlen).
  *
  * Definitions (for b < B, query head h < Hq, KV head g = h / (Hq / Hkv), rows i < Sq, keys j < Sk;
  * the queries are the last Sq positions, query i standing at p = i + Sk - Sq):
@@ -53,15 +56,15 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, size <= 0, Hq % Hkv != 0, window < 0, sink < 0,
-                               non-finite scale, workspace too small */
+                               non-finite scale, workspace too small, n_docs <= 0 */
   ATTN_ERR_UNSUPPORTED = 2, /* D not 64 or 128, unknown dtype, window > 0 without causal,
                                Sq > Sk, B*Hq*Sq*D or B*Hkv*Sk*D >= 2^31, a paged block size
-                               that is not a power of two in [16, 2^20] */
+                               that is not a power of two in [16, 2^20], n_docs > 2047 */
   ATTN_ERR_DEVICE = 3       /* the HIP runtime reported an error for a launch */
 } attn_status_t;
 
@@ -123,6 +126,21 @@ int attn_fwd_paged(int dtype, const void* q, const void* k_pool, const void* v_p
                    const int* block_table, const int* seqlen_k, void* o, float* lse,
                    int B, int Hq, int Hkv, int Sq, int D, int block_size, int max_blocks,
                    int num_blocks, int causal, int window, int sink, float scale, void* stream);
+
+/* Packed documents (causal). Each batch row of q, k, v ([B,Hq,S,D], [B,Hkv,S,D]) holds documents
+ * back to back; cu_seqlens is int32 [B, n_docs + 1] with 0 = c_0 <= c_1 <= ... <= c_n_docs = S
+ * (empty documents allowed; rows with fewer documents repeat S at the end). Key j is visible to
+ * query i of the same row only if both lie in the same document [c_k, c_{k+1}), j <= i, and
+ * (window == 0 || i - j < window). n_docs <= 2047. cu_seqlens is a device array the host does
+ * not read: its values are clamped into [0, S] and a non-monotone array gives unspecified (but
+ * in-bounds) results. Outputs and workspace as attn_fwd / attn_bwd (attn_bwd_workspace_bytes). */
+int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int n_docs, int B, int Hq, int Hkv, int S, int D,
+                    int window, float scale, void* stream);
+int attn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, const int* cu_seqlens, int n_docs,
+                    int B, int Hq, int Hkv, int S, int D, int window, float scale, void* stream);
 
 /* Optional launch observer, for profiling. When set, every entry point calls
  * hook(kernel, 0, stream, user) just before and hook(kernel, 1, stream, user) just after it

@@ -31,8 +31,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_qk", "attn_bwd_qk_workspace_bytes",
-                     "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_paged", "attn_fwd_qk",
-                     "attn_set_launch_hook", "attn_status_string"]
+                     "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_paged",
+                     "attn_fwd_qk", "attn_fwd_varlen", "attn_set_launch_hook", "attn_status_string"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (attn_\w+)", out))
@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fa.attn_abi_version() == 4
+    assert fa.attn_abi_version() == 5
     assert fa.attn_status_string(0) == "ok"
     assert fa.attn_status_string(1) == "invalid argument"
     assert fa.attn_status_string(2) == "unsupported configuration"
@@ -199,6 +199,33 @@ def test_paged_validation(lib):
     assert fwd_paged(lib, sink=-1, window=4) == INV
     assert fwd_paged(lib, causal=0, window=4) == UNS
     assert fwd_paged(lib, D=96) == UNS
+
+
+def test_varlen_validation(lib):
+    INV, UNS = fa.ATTN_ERR_INVALID, fa.ATTN_ERR_UNSUPPORTED
+
+    def fv(ptrs=(P,) * 6, n=3, B=1, Hq=2, Hkv=2, S=64, D=64, window=0, scale=0.125, dtype=1):
+        return lib.attn_fwd_varlen(dtype, *ptrs[:5], ptrs[5], n, B, Hq, Hkv, S, D, window, scale, None)
+
+    for i in range(6):
+        ptrs = [P] * 6
+        ptrs[i] = None
+        assert fv(ptrs=ptrs) == INV
+    assert fv(n=0) == INV
+    assert fv(n=2048) == UNS
+    assert fv(window=-1) == INV
+    assert fv(D=80) == UNS
+    need = fa.attn_bwd_workspace_bytes(1, 2, 2, 64, 64)
+
+    def bv(ws=need, ptrs=(P,) * 11, n=3, S=64):
+        return lib.attn_bwd_varlen(1, *ptrs[:10], ws, ptrs[10], n, 1, 2, 2, S, 64, 0, 0.125, None)
+
+    for i in range(11):
+        ptrs = [P] * 11
+        ptrs[i] = None
+        assert bv(ptrs=ptrs) == INV
+    assert bv(ws=need - 1) == INV
+    assert bv(n=-1) == INV
 
 
 def test_launch_hook_set_and_clear(lib):
