@@ -156,20 +156,35 @@ def cpu_baseline(w, q, k, v, do, heads: int):
 
 
 def bench_paged(w, args, torch, fa) -> int:
-    """Forward against a paged cache (attn_fwd_paged): a step is one forward over the batch."""
+    """Forward only: against a paged cache (attn_fwd_paged, or attn_decode_fwd for decode
+    workloads) or, for dense decode workloads, attn_decode_fwd. A step is one forward over the
+    batch."""
     import numpy as np
     from causal_attention_fa2_amd.workloads import make_inputs, paged_layout
     q, k, v, _ = make_inputs(w)
-    kp, vp, table, lens = paged_layout(w, k, v)
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    tq, tkp, tvp = (torch.from_numpy(x).to(td).cuda() for x in (q, kp, vp))
-    tt, tl = torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
     Sq = w.n_q
+    if w.paged:
+        kp, vp, table, lens = paged_layout(w, k, v)
+        tt, tl = torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
+        max_keys = table.shape[1] * w.paged
+    else:
+        kp, vp, lens = k, v, np.full(w.B, w.S, dtype=np.int32)
+        max_keys = w.S
+    tq, tkp, tvp = (torch.from_numpy(x).to(td).cuda() for x in (q, kp, vp))
     o = torch.empty_like(tq)
     lse = torch.empty((w.B, w.Hq, Sq), dtype=torch.float32, device="cuda")
+    if w.decode:
+        ws = torch.empty(fa.attn_decode_workspace_bytes(w.B, w.Hq, w.Hkv, Sq, max_keys, w.D),
+                         dtype=torch.uint8, device="cuda")
+        extra = dict(block_table=tt, seqlen_k=tl) if w.paged else {}
 
     def step():
-        fa.attn_fwd_paged(tq, tkp, tvp, tt, tl, o, lse, w.causal, w.window, w.scale, None, w.sink)
+        if w.decode:
+            fa.attn_decode_fwd(tq, tkp, tvp, o, lse, ws, w.causal, w.window, w.scale, None, w.sink,
+                               **extra)
+        else:
+            fa.attn_fwd_paged(tq, tkp, tvp, tt, tl, o, lse, w.causal, w.window, w.scale, None, w.sink)
 
     for _ in range(args.warmup):
         step()
@@ -198,12 +213,13 @@ def bench_paged(w, args, torch, fa) -> int:
     value = flops / (ms * 1e-3) / 1e12
     gbs = (kv_bytes + qo_bytes) / (kmed * 1e-3) / 1e9
     out = {
-        "metric": f"paged-cache attention forward TFLOP/s ({w.name})", "value": round(value, 2),
+        "metric": f"attention forward TFLOP/s ({w.name})", "value": round(value, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": Sq, "S_max": w.S,
                    "D": w.D, "block": w.paged, "keys_total": int(lens.sum()), "causal": w.causal,
+                   "path": "attn_decode_fwd" if w.decode else "attn_fwd_paged",
                    "window": w.window, "parallelism": "none (1 GPU)"},
         "kernel_ms_median": round(kmed, 4),
         "roofline": {"kernel": "attn_fwd", "bound": "hbm" if Sq * (w.Hq // w.Hkv) <= 64 else "mfma",
@@ -255,7 +271,7 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     torch.cuda.set_device(0)
-    if w.paged:
+    if w.paged or w.decode:
         return bench_paged(w, args, torch, fa)
     q, k, v, do = make_inputs(w)
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32

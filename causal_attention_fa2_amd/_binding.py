@@ -56,6 +56,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i,
                                    f, vp]
     lib.attn_fwd_paged.restype = i
+    lib.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode_fwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i, i, i, i, i, i,
+                                    i, i, i, i, i, i, f, vp]
+    lib.attn_decode_fwd.restype = i
     lib.attn_fwd_varlen.argtypes = [i, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.attn_fwd_varlen.restype = i
     lib.attn_bwd_varlen.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, i,
@@ -197,6 +202,52 @@ def attn_fwd_paged(q, k_pool, v_pool, block_table, seqlen_k, o, lse, causal: boo
         block_table.shape[1], nb, int(bool(causal)), int(window), int(sink), scale, _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_paged")
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, max_keys: int, D: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, Hq, Hkv, Sq, max_keys, D))
+
+
+def attn_decode_fwd(q, k, v, o, lse, workspace, causal: bool = True, window: int = 0,
+                    scale: float | None = None, stream=None, sink: int = 0, block_table=None,
+                    seqlen_k=None) -> None:
+    """Calls attn_decode_fwd (key-split forward, bf16, (Hq/Hkv)*Sq <= 32). Dense: k/v
+    [B,Hkv,Sk,D]. Paged: k/v pools [num_blocks,Hkv,block_size,D] with block_table int32
+    [B,max_blocks] and seqlen_k int32 [B]. workspace: uint8 tensor of at least
+    attn_decode_workspace_bytes(B, Hq, Hkv, Sq, max_keys, D) bytes (max_keys = Sk, or
+    max_blocks * block_size when paged)."""
+    import torch
+    if not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError("q must be a contiguous GPU tensor")
+    B, Hq, Sq, D = q.shape
+    paged = block_table is not None
+    if paged:
+        nb, Hkv, bs = k.shape[0], k.shape[1], k.shape[2]
+        _check_tensor("k", k, (nb, Hkv, bs, D), q.dtype, q.device)
+        _check_tensor("v", v, (nb, Hkv, bs, D), q.dtype, q.device)
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, max_blocks]")
+        _check_tensor("block_table", block_table, tuple(block_table.shape), torch.int32, q.device)
+        _check_tensor("seqlen_k", seqlen_k, (B,), torch.int32, q.device)
+        Sk, maxb, tptr, lptr = 0, block_table.shape[1], block_table.data_ptr(), seqlen_k.data_ptr()
+    else:
+        Hkv, Sk = k.shape[1], k.shape[2]
+        _check_tensor("k", k, (B, Hkv, Sk, D), q.dtype, q.device)
+        _check_tensor("v", v, (B, Hkv, Sk, D), q.dtype, q.device)
+        nb = bs = maxb = 0
+        tptr = lptr = None
+    _check_tensor("o", o, (B, Hq, Sq, D), q.dtype, q.device)
+    _check_tensor("lse", lse, (B, Hq, Sq), torch.float32, q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    scale = D ** -0.5 if scale is None else float(scale)
+    st = load_library().attn_decode_fwd(
+        _dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(), tptr, lptr, o.data_ptr(),
+        lse.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), B, Hq,
+        Hkv, Sq, Sk, D, bs, maxb, nb, int(bool(causal)), int(window), int(sink), scale,
+        _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_fwd")
 
 
 def _docs_arg(cu_seqlens, B, device):

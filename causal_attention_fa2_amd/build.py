@@ -20,6 +20,7 @@ SOURCES = [
     ("attn_fwd.hip", []),
     ("attn_bwd.hip", []),
     ("attn_dkdv.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("attn_decode.hip", []),
 ]
 
 HIPCC_FLAGS = [

@@ -257,6 +257,61 @@ int attn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, cons
   return fa::launch_bwd(a) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int max_keys, int D) {
+  if (check_common(ATTN_BF16, B, Hq, Hkv, Sq, max_keys, D, 1, 0, 0, 1.0f) != ATTN_OK) return 0;
+  if ((Hq / Hkv) * Sq > 32) return 0;
+  return fa::decode_workspace_bytes(B, Hq, Hkv, Sq, max_keys, D);
+}
+
+int attn_decode_fwd(int dtype, const void* q, const void* k, const void* v, const int* block_table,
+                    const int* seqlen_k, void* o, float* lse, void* workspace,
+                    size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                    int block_size, int max_blocks, int num_blocks, int causal, int window, int sink,
+                    float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return ATTN_ERR_INVALID;
+  const bool paged = block_table != nullptr || seqlen_k != nullptr;
+  if (paged && (!block_table || !seqlen_k)) return ATTN_ERR_INVALID;
+  fa::Args a{};
+  int max_keys = Sk;
+  if (paged) {
+    if (block_size <= 0 || max_blocks <= 0 || num_blocks <= 0) return ATTN_ERR_INVALID;
+    if ((block_size & (block_size - 1)) != 0 || block_size < 16 || block_size > (1 << 20))
+      return ATTN_ERR_UNSUPPORTED;
+    const int64_t capacity = (int64_t)max_blocks * block_size;
+    if (capacity >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+    max_keys = (int)capacity;
+    a.paged = true;
+    a.pg.table = block_table;
+    a.pg.seqlen = seqlen_k;
+    a.pg.shift = __builtin_ctz((unsigned)block_size);
+    a.pg.max_blocks = max_blocks;
+    a.pg.num_blocks = num_blocks;
+  }
+  int st = check_common(dtype, B, Hq, Hkv, Sq, max_keys, D, causal, window, sink, scale);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16 || (Hq / Hkv) * Sq > 32) return ATTN_ERR_UNSUPPORTED;
+  if (workspace_bytes < fa::decode_workspace_bytes(B, Hq, Hkv, Sq, max_keys, D)) return ATTN_ERR_INVALID;
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Sk = max_keys;  // the dense key count; replaced per sequence on the device when paged
+  a.D = D;
+  a.causal = causal;
+  a.window = window;
+  a.sink = sink;
+  a.scale = scale;
+  a.stream = stream;
+  return fa::launch_decode(a, static_cast<float*>(workspace), max_keys) == 0 ? ATTN_OK
+                                                                              : ATTN_ERR_DEVICE;
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -58,6 +58,10 @@ void notify_launch(const char* kernel, int after, void* stream);
 int launch_fwd(const Args& a);
 int launch_bwd(const Args& a);
 int launch_dkdv(const Args& a);  // dK / dV pass (and its reduce), called by launch_bwd
+// Key-split decode forward (bf16, (Hq / Hkv) * Sq <= 32): partials in `part`, then merged into
+// a.o / a.lse. max_keys bounds every sequence's key count (sizes the chunk grid).
+int launch_decode(const Args& a, float* part, int max_keys);
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int max_keys, int D);
 
 // Forward workgroup shape for bf16: waves per workgroup (32 query rows each) and LDS ring depth
 // (tiles in flight + 1).

@@ -24,6 +24,8 @@ measured and checked on; no dataset is involved, every input is synthetic):
                          prefill chunk each (forward only)
   docs-gqa64x8-s8192-d128  one 8192-token buffer of packed documents of U[64, 2048] tokens
                          (the last one cut to fit), Hq=64, Hkv=8, D=128, bf16, causal
+  decode-b1-gqa64x8-k4096  gqa64x8-q1-k4096-d128 through the key-split decode forward
+  decode-paged-b16-gqa64x8  paged-decode-b16-gqa64x8 through the key-split decode forward
 
 Draw order per workload: numpy.random.default_rng(seed); Q, K, V, dO as float32
 standard normals in that order (Q and dO with Sq rows, K and V with S rows) (dO then scaled by its standard deviation); then, for the
@@ -57,6 +59,7 @@ class Workload:
     paged: int = 0  # > 0: K/V in a paged pool of blocks of this many tokens (forward only)
     len_min: int = 0  # paged: sequence b holds U[len_min, S] keys
     docs: tuple = ()  # (min, max): packed documents of U[min, max] tokens per batch row
+    decode: bool = False  # forward only, through the key-split decode forward
 
     @property
     def scale(self) -> float:
@@ -90,6 +93,10 @@ WORKLOADS = {
                  paged=64, len_min=2048),
         Workload("docs-gqa64x8-s8192-d128", 1, 64, 8, 8192, 128, "bf16", True, 0, 1011, do_std=0.1,
                  docs=(64, 2048)),
+        Workload("decode-b1-gqa64x8-k4096", 1, 64, 8, 4096, 128, "bf16", True, 0, 1007, do_std=0.1,
+                 Sq=1, decode=True),
+        Workload("decode-paged-b16-gqa64x8", 16, 64, 8, 8192, 128, "bf16", True, 0, 1009, Sq=1,
+                 paged=16, len_min=1024, decode=True),
     )
 }
 

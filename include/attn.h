@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 typedef enum {
   ATTN_OK = 0,
@@ -142,10 +142,26 @@ int attn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, cons
                     void* workspace, size_t workspace_bytes, const int* cu_seqlens, int n_docs,
                     int B, int Hq, int Hkv, int S, int D, int window, float scale, void* stream);
 
+/* Key-split forward for decode-shaped problems: the same result as attn_fwd_qk (dense k, v
+ * [B,Hkv,Sk,D]; block_table = seqlen_k = NULL) or attn_fwd_paged (block_table, seqlen_k and the
+ * pool arguments as there; Sk is then ignored), up to rounding, computed by many workgroups each
+ * taking 128 keys of one (batch, KV head) for all of its (Hq/Hkv) * Sq query rows, then a merge
+ * of their partial maxima, sums and outputs in a fixed order. Needs bf16 and
+ * (Hq / Hkv) * Sq <= 32 (else ATTN_ERR_UNSUPPORTED). workspace: at least
+ * attn_decode_workspace_bytes(B, Hq, Hkv, Sq, max_keys, D) bytes, max_keys = Sk (dense) or
+ * max_blocks * block_size (paged); returns 0 for unsupported sizes. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int max_keys, int D);
+int attn_decode_fwd(int dtype, const void* q, const void* k, const void* v, const int* block_table,
+                    const int* seqlen_k, void* o, float* lse, void* workspace,
+                    size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                    int block_size, int max_blocks, int num_blocks, int causal, int window,
+                    int sink, float scale, void* stream);
+
 /* Optional launch observer, for profiling. When set, every entry point calls
  * hook(kernel, 0, stream, user) just before and hook(kernel, 1, stream, user) just after it
  * enqueues each of its kernels ("attn_fwd", "attn_bwd_delta", "attn_bwd_dkdv",
- * "attn_bwd_dkdv_reduce" (only when the head group is split), "attn_bwd_dq"),
+ * "attn_bwd_dkdv_reduce" (only when the head group is split), "attn_bwd_dq", "attn_decode",
+ * "attn_decode_combine"),
  * on the calling thread, so the hook can record timing events on `stream` around exactly one
  * kernel. NULL (the default) turns it off. The setting is process-wide; set it while no other
  * thread is calling the library. */

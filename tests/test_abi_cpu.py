@@ -31,8 +31,9 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_qk", "attn_bwd_qk_workspace_bytes",
-                     "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_fwd", "attn_fwd_paged",
-                     "attn_fwd_qk", "attn_fwd_varlen", "attn_set_launch_hook", "attn_status_string"]
+                     "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_fwd",
+                     "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_paged", "attn_fwd_qk",
+                     "attn_fwd_varlen", "attn_set_launch_hook", "attn_status_string"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (attn_\w+)", out))
@@ -42,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fa.attn_abi_version() == 5
+    assert fa.attn_abi_version() == 6
     assert fa.attn_status_string(0) == "ok"
     assert fa.attn_status_string(1) == "invalid argument"
     assert fa.attn_status_string(2) == "unsupported configuration"
@@ -226,6 +227,31 @@ def test_varlen_validation(lib):
         assert bv(ptrs=ptrs) == INV
     assert bv(ws=need - 1) == INV
     assert bv(n=-1) == INV
+
+
+def test_decode_workspace_and_validation(lib):
+    INV, UNS = fa.ATTN_ERR_INVALID, fa.ATTN_ERR_UNSUPPORTED
+    # chunks of 128 keys x B x Hkv x R packed rows x (D + 2) floats
+    assert fa.attn_decode_workspace_bytes(1, 64, 8, 1, 4096, 128) == 32 * 8 * 8 * 130 * 4
+    assert fa.attn_decode_workspace_bytes(2, 8, 2, 3, 300, 64) == 3 * 2 * 2 * 12 * 66 * 4
+    assert fa.attn_decode_workspace_bytes(1, 64, 8, 5, 4096, 128) == 0   # 40 packed rows
+    need = fa.attn_decode_workspace_bytes(1, 64, 8, 1, 4096, 128)
+
+    def dec(ws=need, dtype=1, table=None, lens=None, Hq=64, Sq=1, Sk=4096, bs=0, maxb=0, nb=0, ptrs=(P,) * 6):
+        q, k, v, o, lse, w = ptrs
+        return lib.attn_decode_fwd(dtype, q, k, v, table, lens, o, lse, w, ws, 1, Hq, 8, Sq, Sk, 128, bs,
+                                   maxb, nb, 1, 0, 0, 0.125, None)
+
+    for i in range(6):
+        ptrs = [P] * 6
+        ptrs[i] = None
+        assert dec(ptrs=ptrs) == INV
+    assert dec(ws=need - 1) == INV
+    assert dec(dtype=0) == UNS                 # bf16 only
+    assert dec(Sq=5) == UNS                    # 8 heads x 5 queries > 32 packed rows
+    assert dec(table=P) == INV                 # paged needs both the table and the lengths
+    assert dec(table=P, lens=P, bs=24, maxb=8, nb=4) == UNS
+    assert dec(table=P, lens=P, bs=16, maxb=0, nb=4) == INV
 
 
 def test_launch_hook_set_and_clear(lib):
