@@ -6,8 +6,11 @@
 // the first page (dK and dV of a shared K/V head sum over its query-head group).
 //
 // Launches on the caller's stream, no atomics anywhere:
-//   1. delta_kernel: delta_i = sum_d dO_id * O_id in fp32 (O as the forward stored it), and the
-//      base-2 log-sum-exp lse_i * log2(e) that the gradient kernels exponentiate against.
+//   1. dq_kernel: lanes own queries (as in the forward). Each wave first forms, for its own rows,
+//      delta_i = sum_d dO_id * O_id in fp32 (O as the forward stored it) and the base-2
+//      log-sum-exp lse_i * log2(e), and stores both for the dK / dV pass; then S^T = K Q^T and
+//      dP^T = V dO^T from LDS key/value tiles, dS^T in registers is the B operand of
+//      dQ^T += K^T dS^T with K^T read through the transposing LDS read.
 //   2. dkdv_kernel (attn_dkdv.hip): each wave owns 32 keys whose K and V rows stay in registers as B operands of
 //      S = Q K^T and dP = dO V^T, so a lane owns one key and its accumulator holds query rows --
 //      exactly the contraction side that dV += P^T dO and dK += dS^T Q need. Query / dO / lse /
@@ -18,54 +21,18 @@
 //      few workgroups to fill the GPU, the head group is split into `hs` parts whose fp32 partial
 //      sums go to the workspace and
 //   3. dkdv_reduce_kernel (attn_dkdv.hip) adds them in a fixed order (deterministic) and rounds to the element type.
-//   4. dq_kernel: lanes own queries (as in the forward): S^T = K Q^T and dP^T = V dO^T from LDS
-//      key/value tiles, dS^T in registers is the B operand of dQ^T += K^T dS^T with K^T read
-//      through the transposing LDS read.
 // P and dS are rounded to the element type only as MFMA operands; all sums are fp32.
 #include "device.h"
 #include "launch.h"
 
 namespace fa {
 
-template <class E, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const typename E::T* __restrict__ O,
-                                                    const typename E::T* __restrict__ dO,
-                                                    const float* __restrict__ LSE,
-                                                    float* __restrict__ delta,
-                                                    float* __restrict__ lse2, int rows) {
-  constexpr int TPR = D / 8;       // threads per row, 8 elements each
-  constexpr int RPB = 256 / TPR;   // rows per block
-  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
-  const int part = threadIdx.x % TPR;
-  float s = 0.f;
-  if (row < rows) {
-    const size_t off = (size_t)row * D + part * 8;
-    if constexpr (E::kBytes == 2) {
-      const u32x4_t o = *reinterpret_cast<const u32x4_t*>(O + off);
-      const u32x4_t d = *reinterpret_cast<const u32x4_t*>(dO + off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s += bf16_to_f32(o[e] & 0xFFFFu) * bf16_to_f32(d[e] & 0xFFFFu);
-        s += bf16_to_f32(o[e] >> 16) * bf16_to_f32(d[e] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += O[off + e] * dO[off + e];
-    }
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (part == 0 && row < rows) {
-    delta[row] = s;
-    lse2[row] = LSE[row] * kLog2e;  // base-2 log-sum-exp used by both gradient kernels
-  }
-}
-
 template <class E, int D, int NW, int KB, bool VL>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
-    const float* __restrict__ LSE2, const float* __restrict__ delta, typename E::T* __restrict__ dQ,
+    const typename E::T* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ LSE2,
+    float* __restrict__ delta, typename E::T* __restrict__ dQ,
     int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale,
     float scale_log2, int n_qt, Docs docs) {
   constexpr int BR = 32 * NW;
@@ -137,8 +104,29 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     df[s] = load_frag_global(dO + q_off + (size_t)my_q * D + 16 * s + 8 * half, q_ok);
   }
   const size_t row_idx = (size_t)(b * Hq + h) * Sq + (q_ok ? my_q : 0);
-  const float nlse2 = -LSE2[row_idx];
-  const float dl = delta[row_idx];
+  // delta_i = sum_d dO_id O_id: this lane holds half of row my_q's elements, its partner the rest
+  float dl = 0.f;
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    const Frag<E> of = load_frag_global(O + q_off + (size_t)my_q * D + 16 * s + 8 * half, q_ok);
+    if constexpr (E::kBytes == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dl += bf16_to_f32(of.v[e] & 0xFFFFu) * bf16_to_f32(df[s].v[e] & 0xFFFFu);
+        dl += bf16_to_f32(of.v[e] >> 16) * bf16_to_f32(df[s].v[e] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dl += of.lo[e] * df[s].lo[e] + of.hi[e] * df[s].hi[e];
+    }
+  }
+  dl = pair_sum(dl);
+  const float l2 = LSE[row_idx] * kLog2e;  // base-2 log-sum-exp used by both gradient kernels
+  const float nlse2 = -l2;
+  if (q_ok && half == 0) {
+    delta[row_idx] = dl;
+    LSE2[row_idx] = l2;
+  }
   f32x16_t acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
@@ -225,16 +213,6 @@ static int launch_bwd_t(const Args& a) {
   typedef typename E::T T;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   {
-    const int rows = a.B * a.Hq * a.Sq;
-    constexpr int RPB = 256 / (D / 8);
-    dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
-    notify_launch("attn_bwd_delta", 0, a.stream);
-    hipLaunchKernelGGL((delta_kernel<E, D>), grid, block, 0, st, (const T*)a.o_in, (const T*)a.dout,
-                       (const float*)a.lse, a.delta, a.lse2, rows);
-    notify_launch("attn_bwd_delta", 1, a.stream);
-  }
-  if (launch_dkdv(a) != 0) return -1;
-  {
     constexpr int NW = E::kBytes == 2 ? 8 : 4;
     constexpr int KB = E::kBytes == 2 ? 2 : 1;
     const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
@@ -242,11 +220,13 @@ static int launch_bwd_t(const Args& a) {
     notify_launch("attn_bwd_dq", 0, a.stream);
     auto kern = a.docs.cu ? dq_kernel<E, D, NW, KB, true> : dq_kernel<E, D, NW, KB, false>;
     hipLaunchKernelGGL(kern, grid, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                       (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta, (T*)a.dq, a.B,
-                       a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt,
+                       (const T*)a.dout, (const T*)a.o_in, (const float*)a.lse, a.lse2, a.delta, (T*)a.dq,
+                       a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt,
                        a.docs);
     notify_launch("attn_bwd_dq", 1, a.stream);
   }
+  // the dK / dV pass reads the delta and base-2 log-sum-exp rows that dq_kernel stored
+  if (launch_dkdv(a) != 0) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
