@@ -34,6 +34,7 @@ KERNEL_SOURCES = {
     "attn_bwd_dkdv": ["attn_dkdv.hip", "device.h", "tiles.h"],
     "attn_bwd_dq": ["attn_bwd.hip", "device.h", "tiles.h"],
     "attn_bwd_dkdv_reduce": ["attn_dkdv.hip", "device.h"],
+    "attn_bwd_dkdv_chunks": ["attn_dkdv.hip", "device.h"],
 }
 
 
@@ -279,8 +280,9 @@ def main() -> int:
     o = torch.empty_like(tq)
     lse = torch.empty((w.B, w.Hq, Sq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
-    ws_bytes = fa.attn_bwd_qk_workspace_bytes(w.B, w.Hq, w.Hkv, Sq, w.S, w.D)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws_bytes = fa.attn_bwd_qk_workspace_bytes(w.B, w.Hq, w.Hkv, Sq, w.S, w.D)  # without the sink split
+    ws = torch.empty(fa.attn_bwd_qk_workspace_bytes_for(w.B, w.Hq, w.Hkv, Sq, w.S, w.D, w.causal, w.window,
+                                                        w.sink), dtype=torch.uint8, device="cuda")
     # the square workloads go through attn_fwd / attn_bwd, packed documents through the _varlen
     # entry points, the others through the _qk entry points
     square = Sq == w.S and not w.sink

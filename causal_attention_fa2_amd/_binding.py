@@ -53,6 +53,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_qk.restype = i
     lib.attn_bwd_qk_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_qk_workspace_bytes_for.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.attn_bwd_qk_workspace_bytes_for.restype = ctypes.c_size_t
     lib.attn_fwd_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, i,
                                    f, vp]
     lib.attn_fwd_paged.restype = i
@@ -111,6 +113,13 @@ def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, D: int) -> int:
 
 def attn_bwd_qk_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int) -> int:
     return int(load_library().attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D))
+
+
+def attn_bwd_qk_workspace_bytes_for(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, D: int,
+                                    causal: bool = True, window: int = 0, sink: int = 0) -> int:
+    """Workspace bytes of attn_bwd_qk for these mask arguments (room for the sink split)."""
+    return int(load_library().attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
+                                                               int(window), int(sink)))
 
 
 def _dtype_code(t) -> int:
@@ -355,7 +364,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, window: int = 0,
     B, Hq, Sq, D = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
     if workspace is None:
-        workspace = torch.empty(max(1, attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)),
+        workspace = torch.empty(max(1, attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, causal, window,
+                                                                        sink)),
                                 dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)

@@ -95,6 +95,12 @@ size_t attn_bwd_qk_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D
   return fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D);
 }
 
+size_t attn_bwd_qk_workspace_bytes_for(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                                       int window, int sink) {
+  if (check_common(ATTN_BF16, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, 1.0f) != ATTN_OK) return 0;
+  return fa::bwd_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, causal, window, sink);
+}
+
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
   return attn_bwd_qk_workspace_bytes(B, Hq, Hkv, S, S, D);
 }
@@ -123,6 +129,11 @@ int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const vo
   a.delta = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + row_bytes);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_bytes);
+  // a workspace sized by attn_bwd_qk_workspace_bytes_for holds the sink-split slots after the rest
+  const size_t base_bytes = fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D);
+  const size_t full_bytes = fa::bwd_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, causal, window, sink);
+  if (full_bytes > base_bytes && workspace_bytes >= full_bytes)
+    a.xpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + base_bytes);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

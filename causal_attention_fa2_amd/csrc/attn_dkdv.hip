@@ -287,7 +287,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part, int B, int Hq,
     int Hkv, int Sq, int S, int causal, int window, int sink, float scale, float scale_log2,
-    int n_kt, int n_pairs, int hs, Docs docs) {
+    int n_kt, int n_pairs, int hs, Docs docs, float* __restrict__ xpart, int nc, int c_lo, int c_len) {
   typedef BF16 E;
   constexpr int NW = 8;        // waves
   constexpr int NP = 4;        // wave pairs, 32 keys each
@@ -297,6 +297,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   constexpr int DB = D / 32;
   typedef LdsTile<E, BR, D> QTile;
   constexpr int kTileOps = dma_tile_ops<E, BR, D, NW>();
+  static_assert(BR == kDkdvQueryRows && BC == 32 * kDkdvWaves, "sink-split plan assumes these tiles");
   constexpr int kRowOff = 2 * QTile::kBytes;  // lse[64] then delta[64] (fp32)
   constexpr int kStage = kRowOff + 512;
   constexpr int kPBlock = 2048;  // one 32 x 32 bf16 P block, 32 bytes per lane
@@ -314,11 +315,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   const int pw = w & (NP - 1);
   char* pslot = pbuf + pw * QB * kPBlock + lane * 16;
 
-  // Work item: (batch x KV head, head part, key-tile pair), dealt to XCDs in contiguous chunks.
-  const int T = B * Hkv * hs * n_pairs;
+  // Work item: (batch x KV head, head part, key-tile pair), dealt to XCDs in contiguous chunks;
+  // with a sink split, items T0.. are chunks 1..nc-1 of key tile 0 (batch x KV head, head part).
+  const int BG = B * Hkv;
+  const int T0 = BG * hs * n_pairs;
+  const int T = T0 + (nc - 1) * BG * hs;
   const int wi = (T % 8 == 0) ? (int)(blockIdx.x % 8) * (T / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-  const int pair = wi % n_pairs;
-  const int t2 = wi / n_pairs;
+  const bool extra = wi >= T0;
+  const int e = wi - T0;
+  const int pair = extra ? 0 : wi % n_pairs;
+  const int t2 = extra ? e / (nc - 1) : wi / n_pairs;
+  const int chunk = extra ? 1 + e % (nc - 1) : 0;
   const int hp = t2 % hs;
   const int bg = t2 / hs;
   const int b = bg / Hkv;
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   const int h0 = (bg - b * Hkv) * G + hp * hpg;
   const int ta = pair;
   const int tb = n_kt - 1 - pair;
-  const bool two = tb > ta;
+  const bool two = !extra && tb > ta;
   const size_t kv_off = (size_t)bg * S * D;
   const int qoff = S - Sq;  // query row r stands at key position r + qoff
   if constexpr (VL) {
@@ -342,6 +349,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     kt = t;
     q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, sink, &lo, &hi);
     if constexpr (VL) hi = imin_(hi, (doc_end(cu_s, docs.n, imin_(t * BC + BC - 1, S - 1)) - 1 - qoff) / BR);
+    if (nc > 1 && t == 0) {  // this item's chunk of key tile 0's query tiles
+      lo = c_lo + chunk * c_len;
+      hi = imin_(hi, lo + c_len - 1);
+    }
     nq = imax_(hi - lo + 1, 0);  // 0: no query sees these keys, so dK = dV = 0
     n_steps = hpg * nq;
   };
@@ -377,6 +388,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     const int kw = kt * BC + 32 * pw;
     const size_t nkv = (size_t)B * Hkv * S * D;
     const float mul = srole ? 1.f : scale;
+    // sink split: key tile 0 goes to this chunk's slot [chunk][hp][bg][dK, dV][BC][D]
+    const bool to_x = nc > 1 && kt == 0;
+    float* xs_slot = to_x ? xpart + ((((size_t)chunk * hs + hp) * BG + bg) * 2 + (srole ? 1 : 0)) * BC * D : nullptr;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -384,7 +398,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
         const int key = kw + acc_row(r);
         if (key >= S) continue;
         const size_t o = kv_off + (size_t)key * D + 32 * db + l32;
-        if (hs > 1) {
+        if (to_x) {
+          xs_slot[(size_t)key * D + 32 * db + l32] = acc[db][r];
+        } else if (hs > 1) {
           part[(size_t)(2 * hp + (srole ? 1 : 0)) * nkv + o] = acc[db][r];
         } else {
           (srole ? dV : dK)[o] = (uint16_t)bf16_bits(acc[db][r] * mul);
@@ -522,13 +538,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   }
 }
 
+// Adds the hs head-part partials. Rows below skip_rows of every (batch, KV head) are left to
+// dkdv_chunk_reduce_kernel (their partials live in the sink-split slots instead).
 template <class E>
 __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restrict__ part,
                                                           typename E::T* __restrict__ dK,
                                                           typename E::T* __restrict__ dV,
-                                                          size_t n, int hs, float scale) {
+                                                          size_t n, int hs, float scale, int S, int D,
+                                                          int skip_rows) {
   const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= n) return;
+  if ((int)((i / D) % S) < skip_rows) return;
   f32x4_t sk = *reinterpret_cast<const f32x4_t*>(part + i);
   f32x4_t sv = *reinterpret_cast<const f32x4_t*>(part + n + i);
   for (int p = 1; p < hs; ++p) {
@@ -545,6 +565,32 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
   }
 }
 
+// Sink split: dK / dV of key tile 0 (rows < min(BC, S) of every batch x KV head) = the sum over
+// the nc * hs chunk slots, in a fixed order; dK takes the softmax scale here.
+__global__ __launch_bounds__(256) void dkdv_chunk_reduce_kernel(const float* __restrict__ xpart,
+                                                                uint16_t* __restrict__ dK,
+                                                                uint16_t* __restrict__ dV, int BG,
+                                                                int S, int D, int BC, int parts,
+                                                                float scale) {
+  const int rows = BC < S ? BC : S;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;  // over BG x BC x D
+  const size_t per_bg = (size_t)BC * D;
+  if (i >= (size_t)BG * per_bg) return;
+  const int bg = (int)(i / per_bg);
+  const size_t r = i - (size_t)bg * per_bg;  // key * D + d
+  if ((int)(r / D) >= rows) return;
+  f32x4_t sk = f32x4_t{0.f, 0.f, 0.f, 0.f}, sv = sk;
+  for (int p = 0; p < parts; ++p) {
+    const float* slot = xpart + (((size_t)p * BG + bg) * 2) * per_bg;
+    sk += *reinterpret_cast<const f32x4_t*>(slot + r);
+    sv += *reinterpret_cast<const f32x4_t*>(slot + per_bg + r);
+  }
+  sk *= scale;
+  const size_t o = (size_t)bg * S * D + r;
+  *reinterpret_cast<u32x2_t*>(dK + o) = u32x2_t{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
+  *reinterpret_cast<u32x2_t*>(dV + o) = u32x2_t{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+}
+
 template <class E, int D>
 static int launch_dkdv_t(const Args& a) {
   {
@@ -553,15 +599,18 @@ static int launch_dkdv_t(const Args& a) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     constexpr int NW = kDkdvWaves;
     constexpr int QB = E::kBytes == 2 ? 2 : 1;
-    const DkdvPlan p = dkdv_plan(a.B, a.Hq, a.Hkv, a.Sk);
-    dim3 grid((unsigned)(p.n_pairs * a.B * a.Hkv * p.hs));
+    DkdvPlan p = dkdv_plan(a.B, a.Hq, a.Hkv, a.Sk);
+    if (E::kBytes == 2 && a.xpart != nullptr && !a.docs.cu)
+      dkdv_sink_split(p, a.Sq, a.Sk, a.window, a.sink, a.causal != 0);
+    dim3 grid((unsigned)((p.n_pairs + p.nc - 1) * a.B * a.Hkv * p.hs));
     notify_launch("attn_bwd_dkdv", 0, a.stream);
     if constexpr (E::kBytes == 2) {
       auto kern = a.docs.cu ? dkdv_pair_kernel<D, QB, true> : dkdv_pair_kernel<D, QB, false>;
       hipLaunchKernelGGL(kern, grid, dim3(512), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                          (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta, (T*)a.dk,
                          (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink,
-                         a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs, a.docs);
+                         a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs, a.docs, a.xpart, p.nc, p.c_lo,
+                         p.c_len);
     } else {
       auto kern = a.docs.cu ? dkdv_kernel<E, D, NW, QB, true> : dkdv_kernel<E, D, NW, QB, false>;
       hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, st, (const T*)a.q, (const T*)a.k,
@@ -575,8 +624,20 @@ static int launch_dkdv_t(const Args& a) {
       dim3 rgrid((unsigned)((n / 4 + 255) / 256)), rblock(256);
       notify_launch("attn_bwd_dkdv_reduce", 0, a.stream);
       hipLaunchKernelGGL((dkdv_reduce_kernel<E>), rgrid, rblock, 0, st, (const float*)a.part,
-                         (T*)a.dk, (T*)a.dv, n, p.hs, a.scale);
+                         (T*)a.dk, (T*)a.dv, n, p.hs, a.scale, a.Sk, D, p.nc > 1 ? 32 * kDkdvWaves : 0);
       notify_launch("attn_bwd_dkdv_reduce", 1, a.stream);
+    }
+    if constexpr (E::kBytes == 2) {
+      if (p.nc > 1) {
+        const int BC = 32 * kDkdvWaves;
+        const size_t n = (size_t)a.B * a.Hkv * BC * D;
+        dim3 cgrid((unsigned)((n / 4 + 255) / 256)), cblock(256);
+        notify_launch("attn_bwd_dkdv_chunks", 0, a.stream);
+        hipLaunchKernelGGL(dkdv_chunk_reduce_kernel, cgrid, cblock, 0, st, (const float*)a.xpart,
+                           (uint16_t*)a.dk, (uint16_t*)a.dv, a.B * a.Hkv, a.Sk, D, BC, p.nc * p.hs,
+                           a.scale);
+        notify_launch("attn_bwd_dkdv_chunks", 1, a.stream);
+      }
     }
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

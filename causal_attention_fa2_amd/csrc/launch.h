@@ -4,6 +4,8 @@
 
 #include <stddef.h>
 
+#include "tiles.h"
+
 namespace fa {
 
 enum { kF32 = 0, kBF16 = 1 };
@@ -40,6 +42,7 @@ struct Args {
   void* dv;
   float* delta;       // backward workspace: rowsum(dO * O), [B, Hq, Sq]
   float* lse2;        // backward workspace: lse * log2(e), [B, Hq, Sq]
+  float* xpart;       // backward workspace: sink-split chunk partials, or null (no split)
   float* part;        // backward workspace: fp32 dK / dV partial sums of the head-group parts
   int B, Hq, Hkv, Sq, Sk, D;  // Sq query rows, Sk >= Sq keys (queries: the last Sq positions)
   int causal, window, sink;  // sink: keys [0, sink) stay visible beside the window
@@ -81,6 +84,7 @@ constexpr int kDkdvWaves = 4;
 constexpr int kDkdvMinGroups = 256;
 struct DkdvPlan {
   int n_kt, n_pairs, hs;
+  int nc, c_lo, c_len;  // sink split: key tile 0's query tiles c_lo + [c*c_len, (c+1)*c_len), c < nc
 };
 inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int Sk) {
   DkdvPlan p;
@@ -90,17 +94,56 @@ inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int Sk) {
   const int G = Hq / Hkv;
   p.hs = 1;
   while (items * p.hs < kDkdvMinGroups && G % (2 * p.hs) == 0) p.hs *= 2;
+  p.nc = 1;
+  p.c_lo = 0;
+  p.c_len = 0;
   return p;
+}
+
+// Sink split of the bf16 dK/dV pass. With a window and sink keys (sink <= one key tile), key tile
+// 0 is seen by every later query while any other tile only by about a window's worth, so the
+// workgroup holding tile 0 would run several times longer than the rest. Its query range (tiles
+// of kDkdvQueryRows rows) is cut into nc chunks of about one ordinary tile's range; chunk 0 stays
+// with tile 0's workgroup, chunks 1.. are extra workgroups. Every chunk writes fp32 partial sums of
+// tile 0's dK and dV (per head part) that a small reduce adds in a fixed order.
+constexpr int kDkdvQueryRows = 64;
+constexpr int kDkdvMaxChunks = 16;
+inline void dkdv_sink_split(DkdvPlan& p, int Sq, int Sk, int window, int sink, bool causal) {
+  const int BC = 32 * kDkdvWaves;
+  if (window <= 0 || sink <= 0 || sink > BC) return;
+  const int off = Sk - Sq;
+  const int c1 = (BC < Sk ? BC : Sk) - 1;
+  int lo0, hi0, lo1, hi1;
+  q_tile_range(0, c1, Sk, off, kDkdvQueryRows, causal, window, sink, &lo0, &hi0);
+  q_tile_range(0, c1, Sk, off, kDkdvQueryRows, causal, window, 0, &lo1, &hi1);
+  const int nq0 = hi0 - lo0 + 1;
+  const int nq1 = hi1 >= lo1 ? hi1 - lo1 + 1 : 1;
+  int nc = (nq0 + nq1 - 1) / nq1;
+  if (nc > kDkdvMaxChunks) nc = kDkdvMaxChunks;
+  if (nq0 <= 0 || nc <= 1) return;
+  p.c_lo = lo0;
+  p.c_len = (nq0 + nc - 1) / nc;
+  p.nc = (nq0 + p.c_len - 1) / p.c_len;
+}
+inline size_t dkdv_chunk_bytes(const DkdvPlan& p, int B, int Hkv, int D) {
+  return p.nc > 1 ? (size_t)p.nc * p.hs * B * Hkv * 2 * (32 * kDkdvWaves) * D * sizeof(float) : 0;
 }
 
 inline size_t delta_bytes(int B, int Hq, int Sq) {
   return ((size_t)B * Hq * Sq * sizeof(float) + 255) / 256 * 256;
 }
-// Workspace layout: delta [B,Hq,Sq] f32 | lse * log2(e) [B,Hq,Sq] f32 | dK/dV partials (if split).
+// Workspace layout: delta [B,Hq,Sq] f32 | lse * log2(e) [B,Hq,Sq] f32 | dK/dV partials (if the
+// head group is split) | sink-split chunk partials (when the caller sized the workspace for them).
 inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   const DkdvPlan p = dkdv_plan(B, Hq, Hkv, Sk);
   size_t partials = p.hs > 1 ? (size_t)p.hs * 2 * B * Hkv * Sk * D * sizeof(float) : 0;
   return 2 * delta_bytes(B, Hq, Sq) + partials;
+}
+inline size_t bwd_workspace_bytes_for(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                                      int window, int sink) {
+  DkdvPlan p = dkdv_plan(B, Hq, Hkv, Sk);
+  dkdv_sink_split(p, Sq, Sk, window, sink, causal != 0);
+  return bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) + dkdv_chunk_bytes(p, B, Hkv, D);
 }
 
 }  // namespace fa

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 typedef enum {
   ATTN_OK = 0,
@@ -102,6 +102,17 @@ int attn_fwd_qk(int dtype, const void* q, const void* k, const void* v, void* o,
 /* Workspace bytes of attn_bwd_qk: delta and lse * log2(e) (B*Hq*Sq fp32 each, 256-byte aligned)
  * and, when the head group is split, 2 * parts * B*Hkv*Sk*D fp32. 0 for rejected sizes. */
 size_t attn_bwd_qk_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D);
+
+/* Workspace bytes of attn_bwd_qk for these exact mask arguments: at least
+ * attn_bwd_qk_workspace_bytes(...), plus, with a window and 1 <= sink <= 128 sink keys, room for
+ * the sink split of the bf16 dK/dV pass. Every query past the window still sees the sink keys, so
+ * the first 128-key tile has many times the work of any other; the split shares its query range
+ * among several workgroups whose fp32 partial sums (2 * chunks * parts * B*Hkv*128*D) a small
+ * reduce adds in a fixed order. attn_bwd_qk uses the split only when workspace_bytes is at least
+ * this size (otherwise it runs unsplit, same results up to summation order). 0 for rejected
+ * sizes. */
+size_t attn_bwd_qk_workspace_bytes_for(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                                       int window, int sink);
 
 /* Backward with Sq queries against Sk >= Sq keys and `sink` sink keys. dout, dq are
  * [B,Hq,Sq,D]; dk, dv [B,Hkv,Sk,D] (keys no query sees get exact zeros). Same contract as

@@ -31,6 +31,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_qk", "attn_bwd_qk_workspace_bytes",
+                     "attn_bwd_qk_workspace_bytes_for",
                      "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_fwd",
                      "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_paged", "attn_fwd_qk",
                      "attn_fwd_varlen", "attn_set_launch_hook", "attn_status_string"]
@@ -43,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fa.attn_abi_version() == 6
+    assert fa.attn_abi_version() == 7
     assert fa.attn_status_string(0) == "ok"
     assert fa.attn_status_string(1) == "invalid argument"
     assert fa.attn_status_string(2) == "unsupported configuration"
@@ -89,6 +90,50 @@ def test_qk_workspace_bytes(lib):
     assert fa.attn_bwd_qk_workspace_bytes(1, 2, 2, 65, 64, 64) == 0  # more queries than keys
     assert fa.attn_bwd_qk_workspace_bytes(1, 2, 2, 0, 64, 64) == 0
     assert fa.attn_bwd_qk_workspace_bytes(1, 2, 2, 64, 0, 64) == 0
+
+
+def _sink_chunks(Sq, Sk, window, sink):
+    """Chunks of key tile 0's query range in the sink split (query tiles of 64 rows): enough
+    chunks of about one ordinary tile's range each, at most 16; 1 = no split."""
+    if window <= 0 or sink <= 0 or sink > 128:
+        return 1
+    off, c1 = Sk - Sq, min(128, Sk) - 1
+
+    def rng(s):  # query tiles holding a row that sees some key in [0, c1] (causal)
+        lo = max(0, off) - off
+        hi = (Sk - 1 if s > 0 else min(Sk - 1, c1 + window - 1)) - off
+        return (lo // 64, hi // 64) if hi >= lo else (1, 0)
+    lo0, hi0 = rng(sink)
+    lo1, hi1 = rng(0)
+    nq0, nq1 = hi0 - lo0 + 1, max(hi1 - lo1 + 1, 1)
+    nc = min(-(-nq0 // nq1), 16)
+    if nq0 <= 0 or nc <= 1:
+        return 1
+    c_len = -(-nq0 // nc)
+    return -(-nq0 // c_len)
+
+
+def test_qk_workspace_bytes_for(lib):
+    """Without a window or without sinks it is attn_bwd_qk_workspace_bytes; with both it adds the
+    chunk slots: 2 (dK, dV) x chunks x head parts x B*Hkv x 128 keys x D fp32."""
+    for B, Hq, Hkv, Sq, Sk, D, window, sink in ((1, 64, 8, 8192, 8192, 128, 1024, 4),
+                                                (1, 8, 2, 1024, 1024, 128, 128, 4),
+                                                (2, 4, 2, 300, 700, 64, 50, 1),
+                                                (1, 64, 8, 4096, 4096, 128, 0, 4),
+                                                (1, 64, 8, 4096, 4096, 128, 256, 0),
+                                                (1, 4, 2, 640, 640, 128, 70, 130)):
+        base = fa.attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+        nc = _sink_chunks(Sq, Sk, window, sink)
+        extra = 2 * nc * _parts(B, Hq, Hkv, Sk) * B * Hkv * 128 * D * 4 if nc > 1 else 0
+        got = fa.attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, True, window, sink)
+        assert got == base + extra, (B, Hq, Hkv, Sq, Sk, D, window, sink, nc)
+    # the sliding-window workload with 4 sinks: tile 0 is seen by all 128 query tiles, any other
+    # tile by 18, so 8 chunks of 16
+    assert _sink_chunks(8192, 8192, 1024, 4) == 8
+    assert fa.attn_bwd_qk_workspace_bytes_for(1, 64, 8, 8192, 8192, 128, True, 1024, 4) == \
+        fa.attn_bwd_qk_workspace_bytes(1, 64, 8, 8192, 8192, 128) + 2 * 8 * 8 * 128 * 128 * 4
+    assert fa.attn_bwd_qk_workspace_bytes_for(1, 2, 2, 65, 64, 64, True, 8, 1) == 0  # rejected
+    assert fa.attn_bwd_qk_workspace_bytes_for(1, 2, 2, 64, 64, 64, True, 8, -1) == 0
 
 
 P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first

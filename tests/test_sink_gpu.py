@@ -133,3 +133,38 @@ def test_sink_workload_full_size_sampled():
     ev = np.sqrt(np.sum((got["dV"].sum(axis=2) - want) ** 2)) / np.sqrt(np.sum(got["dV"] ** 2))
     say(f"  identities {w.name}: |sum dK|/|dK|={ek:.2e} |sum dV - sum dO|/|dV|={ev:.2e}")
     assert ek <= 2e-2 and ev <= 2e-2
+
+
+def test_sink_split_matches_unsplit():
+    """The sink split of the dK/dV pass (workspace sized by attn_bwd_qk_workspace_bytes_for) against
+    the unsplit pass (workspace of attn_bwd_qk_workspace_bytes) and the oracle. Hq/Hkv = 4 with
+    B*Hkv = 2 also splits the head group (4 parts), so both reduces run. dQ and the dK/dV rows past
+    the first 128-key tile do not depend on the split (bit-identical); the first tile's rows differ
+    only in the order of their fp32 partial sums."""
+    import torch
+    import causal_attention_fa2_amd as fa
+    from gpu_util import download, upload
+    dtype, B, Hq, Hkv, S, D, window, sink = "bf16", 1, 8, 2, 1024, 128, 128, 4
+    base = fa.attn_bwd_qk_workspace_bytes(B, Hq, Hkv, S, S, D)
+    full = fa.attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, S, S, D, True, window, sink)
+    assert full > base
+    say(f"sink split B={B} Hq={Hq} Hkv={Hkv} S={S} window={window} sink={sink}: {base} / {full} bytes")
+    q, k, v, do = _inputs(dtype, B, Hq, Hkv, S, S, D, seed=77)
+    scale = 1.0 / math.sqrt(D)
+    tq, tk, tv, tdo = (upload(x, dtype) for x in (q, k, v, do))
+    o, lse = fa.forward(tq, tk, tv, True, window, scale, sink=sink)
+    res = {}
+    for name, nbytes in (("unsplit", base), ("split", full)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dq, dk, dv = fa.backward(tq, tk, tv, o, lse, tdo, True, window, scale, workspace=ws, sink=sink)
+        torch.cuda.synchronize()
+        res[name] = {"dQ": download(dq), "dK": download(dk), "dV": download(dv)}
+    ref = oracle.forward_backward(q, k, v, do, True, window, scale, sink=sink)
+    for name, got in res.items():
+        assert_parity(got, ref, dtype, names=("dQ", "dK", "dV"), tag=name)
+    assert np.array_equal(res["split"]["dQ"], res["unsplit"]["dQ"])
+    for n in ("dK", "dV"):
+        a, b = res["split"][n], res["unsplit"][n]
+        assert np.array_equal(a[:, :, 128:], b[:, :, 128:]), n
+        # first tile: the same fp32 sums in another order, then one rounding to bf16
+        assert np.allclose(a[:, :, :128], b[:, :, :128], rtol=2.0 ** -7, atol=1e-6 * np.abs(b).max()), n
