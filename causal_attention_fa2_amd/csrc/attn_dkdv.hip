@@ -317,10 +317,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
 
   // Work item: (batch x KV head, head part, key-tile pair), dealt to XCDs in contiguous chunks;
   // with a sink split, items T0.. are chunks 1..nc-1 of key tile 0 (batch x KV head, head part).
+  // (the chunk items, which are smaller, follow in launch order and spread over all XCDs)
   const int BG = B * Hkv;
   const int T0 = BG * hs * n_pairs;
-  const int T = T0 + (nc - 1) * BG * hs;
-  const int wi = (T % 8 == 0) ? (int)(blockIdx.x % 8) * (T / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int bx = (int)blockIdx.x;
+  const int wi = (bx < T0 && T0 % 8 == 0) ? (bx % 8) * (T0 / 8) + bx / 8 : bx;
   const bool extra = wi >= T0;
   const int e = wi - T0;
   const int pair = extra ? 0 : wi % n_pairs;
@@ -601,7 +602,7 @@ static int launch_dkdv_t(const Args& a) {
     constexpr int QB = E::kBytes == 2 ? 2 : 1;
     DkdvPlan p = dkdv_plan(a.B, a.Hq, a.Hkv, a.Sk);
     if (E::kBytes == 2 && a.xpart != nullptr && !a.docs.cu)
-      dkdv_sink_split(p, a.Sq, a.Sk, a.window, a.sink, a.causal != 0);
+      dkdv_sink_split(p, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.window, a.sink, a.causal != 0);
     dim3 grid((unsigned)((p.n_pairs + p.nc - 1) * a.B * a.Hkv * p.hs));
     notify_launch("attn_bwd_dkdv", 0, a.stream);
     if constexpr (E::kBytes == 2) {

@@ -102,13 +102,17 @@ inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int Sk) {
 
 // Sink split of the bf16 dK/dV pass. With a window and sink keys (sink <= one key tile), key tile
 // 0 is seen by every later query while any other tile only by about a window's worth, so the
-// workgroup holding tile 0 would run several times longer than the rest. Its query range (tiles
-// of kDkdvQueryRows rows) is cut into nc chunks of about one ordinary tile's range; chunk 0 stays
-// with tile 0's workgroup, chunks 1.. are extra workgroups. Every chunk writes fp32 partial sums of
-// tile 0's dK and dV (per head part) that a small reduce adds in a fixed order.
+// workgroup holding tile 0 would run several times longer than the rest. When that workgroup
+// would outlast the average load of a compute unit, its query range (tiles of kDkdvQueryRows
+// rows) is cut into nc chunks of about a quarter of an ordinary tile's range: chunk 0 stays with
+// tile 0's workgroup, chunks 1.. become small extra workgroups that fill in behind the ordinary
+// ones. Every chunk writes fp32 partial sums of tile 0's dK and dV (per head part) that a small
+// reduce adds in a fixed order.
 constexpr int kDkdvQueryRows = 64;
-constexpr int kDkdvMaxChunks = 16;
-inline void dkdv_sink_split(DkdvPlan& p, int Sq, int Sk, int window, int sink, bool causal) {
+constexpr int kDkdvMaxChunks = 64;
+constexpr int kComputeUnits = 256;  // MI355X
+inline void dkdv_sink_split(DkdvPlan& p, int B, int Hq, int Hkv, int Sq, int Sk, int window, int sink,
+                            bool causal) {
   const int BC = 32 * kDkdvWaves;
   if (window <= 0 || sink <= 0 || sink > BC) return;
   const int off = Sk - Sq;
@@ -118,11 +122,16 @@ inline void dkdv_sink_split(DkdvPlan& p, int Sq, int Sk, int window, int sink, b
   q_tile_range(0, c1, Sk, off, kDkdvQueryRows, causal, window, 0, &lo1, &hi1);
   const int nq0 = hi0 - lo0 + 1;
   const int nq1 = hi1 >= lo1 ? hi1 - lo1 + 1 : 1;
-  int nc = (nq0 + nq1 - 1) / nq1;
-  if (nc > kDkdvMaxChunks) nc = kDkdvMaxChunks;
-  if (nq0 <= 0 || nc <= 1) return;
+  if (nq0 <= nq1) return;
+  // steps (query tiles x heads of a part) of tile 0's workgroup against a compute unit's share
+  const long hpg = Hq / Hkv / p.hs;
+  const long heavy = (long)(nq0 + nq1) * hpg;
+  const long share = (long)B * Hkv * p.hs * p.n_pairs * 2 * nq1 * hpg / kComputeUnits;
+  if (heavy * 10 <= share * 11) return;
+  p.c_len = (nq1 + 3) / 4;
+  int nc = (nq0 + p.c_len - 1) / p.c_len;
+  if (nc > kDkdvMaxChunks) p.c_len = (nq0 + kDkdvMaxChunks - 1) / kDkdvMaxChunks;
   p.c_lo = lo0;
-  p.c_len = (nq0 + nc - 1) / nc;
   p.nc = (nq0 + p.c_len - 1) / p.c_len;
 }
 inline size_t dkdv_chunk_bytes(const DkdvPlan& p, int B, int Hkv, int D) {
@@ -142,7 +151,7 @@ inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D)
 inline size_t bwd_workspace_bytes_for(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
                                       int window, int sink) {
   DkdvPlan p = dkdv_plan(B, Hq, Hkv, Sk);
-  dkdv_sink_split(p, Sq, Sk, window, sink, causal != 0);
+  dkdv_sink_split(p, B, Hq, Hkv, Sq, Sk, window, sink, causal != 0);
   return bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) + dkdv_chunk_bytes(p, B, Hkv, D);
 }
 
