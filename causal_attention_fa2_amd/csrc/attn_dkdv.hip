@@ -306,6 +306,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   __shared__ __attribute__((aligned(1024))) char st2[kStage];
   __shared__ __attribute__((aligned(1024))) char pbuf[NP * QB * kPBlock];
   __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
+  __shared__ int tile_cost[VL ? kBalancedTiles : 1];
+  __shared__ int tile_order[VL ? kBalancedTiles : 1];
 
   const int lane = lane_id();
   const int w = wave_id();
@@ -333,8 +335,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   const int G = Hq / Hkv;
   const int hpg = G / hs;
   const int h0 = (bg - b * Hkv) * G + hp * hpg;
-  const int ta = pair;
-  const int tb = n_kt - 1 - pair;
+  int ta = pair;
+  int tb = n_kt - 1 - pair;
   const bool two = !extra && tb > ta;
   const size_t kv_off = (size_t)bg * S * D;
   const int qoff = S - Sq;  // query row r stands at key position r + qoff
@@ -344,17 +346,50 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   }
   int de_lane = 0;  // documents: end of this lane's key's document (rows at or past it cannot see it)
 
+  // Query tiles that key tile t's segment streams: [*lo, *lo + return value).
+  auto tile_queries = [&](int t, int* lo) __attribute__((always_inline)) {
+    int hi;
+    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, sink, lo, &hi);
+    if constexpr (VL) hi = imin_(hi, (doc_end(cu_s, docs.n, imin_(t * BC + BC - 1, S - 1)) - 1 - qoff) / BR);
+    return imax_(hi - *lo + 1, 0);
+  };
+  if constexpr (VL) {
+    // Packed documents: a key tile's work depends on where it lies in its document, so the
+    // pairing of tile j with tile n_kt-1-j no longer balances. Every workgroup ranks the tiles by
+    // their query-tile count (ties by index: the same order everywhere) and pair p takes the p-th
+    // heaviest and the p-th lightest. Up to kBalancedTiles tiles; longer rows keep the plain pairing.
+    if (n_kt <= kBalancedTiles) {
+      for (int t = threadIdx.x; t < n_kt; t += blockDim.x) {
+        int l0;
+        tile_cost[t] = tile_queries(t, &l0);
+      }
+      __syncthreads();
+      for (int t = threadIdx.x; t < n_kt; t += blockDim.x) {
+        const int c = tile_cost[t];
+        int rank = 0;
+        for (int u = 0; u < n_kt; ++u) {
+          const int cu = tile_cost[u];
+          rank += (cu > c || (cu == c && u < t)) ? 1 : 0;
+        }
+        tile_order[rank] = t;
+      }
+      __syncthreads();
+      if (!extra) {
+        ta = tile_order[pair];
+        tb = tile_order[n_kt - 1 - pair];
+      }
+    }
+  }
+
   int kt = ta, lo = 0, nq = 0, n_steps = 0;
   auto set_segment = [&](int t) __attribute__((always_inline)) {
-    int hi;
     kt = t;
-    q_tile_range(t * BC, imin_(t * BC + BC - 1, S - 1), S, qoff, BR, causal, window, sink, &lo, &hi);
-    if constexpr (VL) hi = imin_(hi, (doc_end(cu_s, docs.n, imin_(t * BC + BC - 1, S - 1)) - 1 - qoff) / BR);
+    nq = tile_queries(t, &lo);  // 0: no query sees these keys, so dK = dV = 0
     if (nc > 1 && t == 0) {  // this item's chunk of key tile 0's query tiles
+      const int hi = lo + nq - 1;
       lo = c_lo + chunk * c_len;
-      hi = imin_(hi, lo + c_len - 1);
+      nq = imax_(imin_(hi, lo + c_len - 1) - lo + 1, 0);
     }
-    nq = imax_(hi - lo + 1, 0);  // 0: no query sees these keys, so dK = dV = 0
     n_steps = hpg * nq;
   };
   // Query tiles run from the last one down, head by head; (hh, it) = head offset, tile counter.

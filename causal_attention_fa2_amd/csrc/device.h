@@ -449,6 +449,9 @@ __device__ __forceinline__ void stage_docs(int* dst, const int* __restrict__ src
   for (int t = threadIdx.x; t <= n; t += blockDim.x) dst[t] = imin_(imax_(src[t], 0), S);
 }
 
+// Packed documents: at most this many key tiles are ranked by work in the dK/dV pass.
+constexpr int kBalancedTiles = 256;
+
 // Accumulator row index (within a 32 x 32 tile) held in register r by this lane.
 __device__ __forceinline__ int acc_row(int r) { return 8 * (r >> 2) + 4 * (lane_id() >> 5) + (r & 3); }
 
