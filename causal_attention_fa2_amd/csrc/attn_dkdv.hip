@@ -602,29 +602,44 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* __restric
 }
 
 // Sink split: dK / dV of key tile 0 (rows < min(BC, S) of every batch x KV head) = the sum over
-// the nc * hs chunk slots, in a fixed order; dK takes the softmax scale here.
+// the nc * hs chunk slots, in a fixed order; dK takes the softmax scale here. One element per
+// thread, slots read four at a time.
 __global__ __launch_bounds__(256) void dkdv_chunk_reduce_kernel(const float* __restrict__ xpart,
                                                                 uint16_t* __restrict__ dK,
                                                                 uint16_t* __restrict__ dV, int BG,
                                                                 int S, int D, int BC, int parts,
                                                                 float scale) {
   const int rows = BC < S ? BC : S;
-  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;  // over BG x BC x D
   const size_t per_bg = (size_t)BC * D;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // over BG x BC x D
   if (i >= (size_t)BG * per_bg) return;
   const int bg = (int)(i / per_bg);
   const size_t r = i - (size_t)bg * per_bg;  // key * D + d
   if ((int)(r / D) >= rows) return;
-  f32x4_t sk = f32x4_t{0.f, 0.f, 0.f, 0.f}, sv = sk;
-  for (int p = 0; p < parts; ++p) {
-    const float* slot = xpart + (((size_t)p * BG + bg) * 2) * per_bg;
-    sk += *reinterpret_cast<const f32x4_t*>(slot + r);
-    sv += *reinterpret_cast<const f32x4_t*>(slot + per_bg + r);
+  const size_t stride = (size_t)BG * 2 * per_bg;  // from one slot to the next
+  const float* pk = xpart + (size_t)bg * 2 * per_bg + r;
+  float sk = 0.f, sv = 0.f;
+  int p = 0;
+  for (; p + 4 <= parts; p += 4) {
+    float k4[4], v4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      k4[u] = pk[(size_t)(p + u) * stride];
+      v4[u] = pk[(size_t)(p + u) * stride + per_bg];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sk += k4[u];
+      sv += v4[u];
+    }
   }
-  sk *= scale;
+  for (; p < parts; ++p) {
+    sk += pk[(size_t)p * stride];
+    sv += pk[(size_t)p * stride + per_bg];
+  }
   const size_t o = (size_t)bg * S * D + r;
-  *reinterpret_cast<u32x2_t*>(dK + o) = u32x2_t{pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
-  *reinterpret_cast<u32x2_t*>(dV + o) = u32x2_t{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+  dK[o] = (uint16_t)bf16_bits(sk * scale);
+  dV[o] = (uint16_t)bf16_bits(sv);
 }
 
 template <class E, int D>
@@ -667,7 +682,7 @@ static int launch_dkdv_t(const Args& a) {
       if (p.nc > 1) {
         const int BC = 32 * kDkdvWaves;
         const size_t n = (size_t)a.B * a.Hkv * BC * D;
-        dim3 cgrid((unsigned)((n / 4 + 255) / 256)), cblock(256);
+        dim3 cgrid((unsigned)((n + 255) / 256)), cblock(256);
         notify_launch("attn_bwd_dkdv_chunks", 0, a.stream);
         hipLaunchKernelGGL(dkdv_chunk_reduce_kernel, cgrid, cblock, 0, st, (const float*)a.xpart,
                            (uint16_t*)a.dk, (uint16_t*)a.dv, a.B * a.Hkv, a.Sk, D, BC, p.nc * p.hs,
