@@ -29,12 +29,12 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "fwd+bwd causal attn TFLOP/s & % bf16 MFMA peak (GQA 64/8, d128, S=4096)"
-KERNEL_SOURCES = {
-    "attn_fwd": ["attn_fwd.hip", "device.h", "tiles.h"],
-    "attn_bwd_dkdv": ["attn_dkdv.hip", "device.h", "tiles.h"],
-    "attn_bwd_dq": ["attn_bwd.hip", "device.h", "tiles.h"],
-    "attn_bwd_dkdv_reduce": ["attn_dkdv.hip", "device.h"],
-    "attn_bwd_dkdv_chunks": ["attn_dkdv.hip", "device.h"],
+KERNEL_SOURCES = {  # the files a kernel's code and launch configuration come from
+    "attn_fwd": ["attn_fwd.hip", "device.h", "tiles.h", "launch.h"],
+    "attn_bwd_dkdv": ["attn_dkdv.hip", "device.h", "tiles.h", "launch.h"],
+    "attn_bwd_dq": ["attn_bwd.hip", "device.h", "tiles.h", "launch.h"],
+    "attn_bwd_dkdv_reduce": ["attn_dkdv.hip", "device.h", "launch.h"],
+    "attn_bwd_dkdv_chunks": ["attn_dkdv.hip", "device.h", "launch.h"],
 }
 
 

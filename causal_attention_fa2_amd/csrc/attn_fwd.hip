@@ -237,6 +237,8 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   if (half == 0) LSE[(size_t)(b * Hq + h) * Sq + my_q] = (m + __log2f(l)) * kLn2;
 }
 
+// Ring depth: bf16 two stages (one tile in flight; measured about 1% faster than three at
+// S = 4096 and no different on the S_q = 1024 / 1 shapes), f32 three.
 template <class E, int D>
 static int launch_fwd_t(const Args& a) {
   constexpr int NW = E::kBytes == 2 ? kFwdWaves : 4;

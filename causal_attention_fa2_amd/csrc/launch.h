@@ -72,7 +72,7 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int max_keys, int 
 #define ATTN_FWD_WAVES 8
 #endif
 #ifndef ATTN_FWD_STAGES
-#define ATTN_FWD_STAGES 3
+#define ATTN_FWD_STAGES 2
 #endif
 constexpr int kFwdWaves = ATTN_FWD_WAVES, kFwdStages = ATTN_FWD_STAGES;
 
