@@ -135,21 +135,30 @@ def test_sink_workload_full_size_sampled():
     assert ek <= 2e-2 and ev <= 2e-2
 
 
-def test_sink_split_matches_unsplit():
+SPLIT_CASES = [
+    # B, Hq, Hkv, S, D, window, sink: head group split in 4 / two batch rows / S not a multiple of 128
+    (1, 8, 2, 1024, 128, 128, 4),
+    (2, 4, 2, 768, 64, 64, 2),
+    (1, 4, 4, 600, 128, 100, 1),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_sink_split_matches_unsplit(case):
     """The sink split of the dK/dV pass (workspace sized by attn_bwd_qk_workspace_bytes_for) against
-    the unsplit pass (workspace of attn_bwd_qk_workspace_bytes) and the oracle. Hq/Hkv = 4 with
-    B*Hkv = 2 also splits the head group (4 parts), so both reduces run. dQ and the dK/dV rows past
-    the first 128-key tile do not depend on the split (bit-identical); the first tile's rows differ
-    only in the order of their fp32 partial sums."""
+    the unsplit pass (workspace of attn_bwd_qk_workspace_bytes) and the oracle. dQ and the dK/dV
+    rows past the first 128-key tile do not depend on the split (bit-identical); the first tile's
+    rows differ only in the order of their fp32 partial sums."""
     import torch
     import causal_attention_fa2_amd as fa
     from gpu_util import download, upload
-    dtype, B, Hq, Hkv, S, D, window, sink = "bf16", 1, 8, 2, 1024, 128, 128, 4
+    B, Hq, Hkv, S, D, window, sink = case
+    dtype = "bf16"
     base = fa.attn_bwd_qk_workspace_bytes(B, Hq, Hkv, S, S, D)
     full = fa.attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, S, S, D, True, window, sink)
-    assert full > base
-    say(f"sink split B={B} Hq={Hq} Hkv={Hkv} S={S} window={window} sink={sink}: {base} / {full} bytes")
-    q, k, v, do = _inputs(dtype, B, Hq, Hkv, S, S, D, seed=77)
+    assert full > base  # these shapes split
+    say(f"sink split {case}: {base} / {full} bytes")
+    q, k, v, do = _inputs(dtype, B, Hq, Hkv, S, S, D, seed=77 + S)
     scale = 1.0 / math.sqrt(D)
     tq, tk, tv, tdo = (upload(x, dtype) for x in (q, k, v, do))
     o, lse = fa.forward(tq, tk, tv, True, window, scale, sink=sink)
