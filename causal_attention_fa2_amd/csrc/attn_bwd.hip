@@ -214,7 +214,7 @@ static int launch_bwd_t(const Args& a) {
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   {
     constexpr int NW = E::kBytes == 2 ? 8 : 4;
-    constexpr int KB = E::kBytes == 2 ? 2 : 1;
+    constexpr int KB = E::kBytes == 2 ? (D == 64 ? 4 : 2) : 1;  // 128-key tiles for D = 64 (3% faster)
     const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
     dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
     notify_launch("attn_bwd_dq", 0, a.stream);
