@@ -297,9 +297,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   constexpr int DB = D / 32;
   typedef LdsTile<E, BR, D> QTile;
   constexpr int kTileOps = dma_tile_ops<E, BR, D, NW>();
-  static_assert(BR == kDkdvQueryRows && BC == 32 * kDkdvWaves, "sink-split plan assumes these tiles");
-  constexpr int kRowOff = 2 * QTile::kBytes;  // lse[64] then delta[64] (fp32)
-  constexpr int kStage = kRowOff + 512;
+  static_assert(BR == dkdv_query_rows(D) && BC == 32 * kDkdvWaves, "the host plan assumes these tiles");
+  static_assert(BR % 64 == 0 && 2 * (BR / 64) <= NW, "one row copy (64 floats) per wave");
+  constexpr int kRowOff = 2 * QTile::kBytes;  // lse[BR] then delta[BR] (fp32)
+  constexpr int kRowWaves = 2 * (BR / 64);      // waves that copy 64 of those floats per tile
+  constexpr int kStage = kRowOff + 8 * BR;
   constexpr int kPBlock = 2048;  // one 32 x 32 bf16 P block, 32 bytes per lane
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
@@ -398,8 +400,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     const size_t bh = (size_t)b * Hq + h0 + hh;
     dma_tile<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, Sq);
     dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, Sq);
-    if (w == 0) dma_row_floats(stg + kRowOff, LSE2 + bh * Sq, i0, Sq);
-    if (w == 1) dma_row_floats(stg + kRowOff + 256, delta + bh * Sq, i0, Sq);
+    if (w < kRowWaves) {  // wave 2c copies lse rows 64c.., wave 2c+1 the delta rows 64c..
+      const int c = w >> 1;
+      dma_row_floats(stg + kRowOff + (w & 1) * 4 * BR + 256 * c, ((w & 1) ? delta : LSE2) + bh * Sq, i0 + 64 * c, Sq);
+    }
   };
   auto advance = [&](int& hh, int& it) __attribute__((always_inline)) {
     if (++it == nq) {
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   auto compute = [&](int it, const char* q_lds) __attribute__((always_inline)) {
     const char* do_lds = q_lds + QTile::kBytes;
     const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
-    const float* dl_lds = lse_lds + 64;
+    const float* dl_lds = lse_lds + BR;
     const int i0 = (lo + nq - 1 - it) * BR;
     const int p0 = i0 + qoff;  // position of the tile's first row
     const int kw = kt * BC + 32 * pw;
@@ -537,7 +541,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
     char* nn = ST == 0 ? st2 : (ST == 1 ? st0 : st1);
     if (s + 1 < n_steps) {
-      if (w < 2) wait_vmcnt<2 * kTileOps + 1>();
+      if (w < kRowWaves) wait_vmcnt<2 * kTileOps + 1>();
       else wait_vmcnt<2 * kTileOps>();
     } else {
       wait_vmcnt<0>();
@@ -649,10 +653,10 @@ static int launch_dkdv_t(const Args& a) {
     typedef typename E::T T;
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     constexpr int NW = kDkdvWaves;
-    constexpr int QB = E::kBytes == 2 ? 2 : 1;
+    constexpr int QB = E::kBytes == 2 ? dkdv_query_rows(D) / 32 : 1;
     DkdvPlan p = dkdv_plan(a.B, a.Hq, a.Hkv, a.Sk);
     if (E::kBytes == 2 && a.xpart != nullptr && !a.docs.cu)
-      dkdv_sink_split(p, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.window, a.sink, a.causal != 0);
+      dkdv_sink_split(p, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, D, a.window, a.sink, a.causal != 0);
     dim3 grid((unsigned)((p.n_pairs + p.nc - 1) * a.B * a.Hkv * p.hs));
     notify_launch("attn_bwd_dkdv", 0, a.stream);
     if constexpr (E::kBytes == 2) {

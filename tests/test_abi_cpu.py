@@ -92,19 +92,20 @@ def test_qk_workspace_bytes(lib):
     assert fa.attn_bwd_qk_workspace_bytes(1, 2, 2, 64, 0, 64) == 0
 
 
-def _sink_chunks(B, Hq, Hkv, Sq, Sk, window, sink):
-    """Chunks of key tile 0's query range in the sink split (query tiles of 64 rows, 1 = no split):
+def _sink_chunks(B, Hq, Hkv, Sq, Sk, D, window, sink):
+    """Chunks of key tile 0's query range in the sink split (query tiles of 64 rows, 128 for
+    D = 64; 1 = no split):
     only when tile 0's workgroup (its range plus an ordinary tile's, times the heads of a part)
     would exceed 1.1x a compute unit's share of the work (256 units); chunks of a quarter of an
     ordinary tile's range, at most 64 of them."""
     if window <= 0 or sink <= 0 or sink > 128:
         return 1
-    off, c1 = Sk - Sq, min(128, Sk) - 1
+    off, c1, br = Sk - Sq, min(128, Sk) - 1, 128 if D == 64 else 64
 
     def rng(s):  # query tiles holding a row that sees some key in [0, c1] (causal)
         lo = max(0, off) - off
         hi = (Sk - 1 if s > 0 else min(Sk - 1, c1 + window - 1)) - off
-        return (lo // 64, hi // 64) if hi >= lo else (1, 0)
+        return (lo // br, hi // br) if hi >= lo else (1, 0)
     lo0, hi0 = rng(sink)
     lo1, hi1 = rng(0)
     nq0, nq1 = hi0 - lo0 + 1, max(hi1 - lo1 + 1, 1)
@@ -131,18 +132,20 @@ def test_qk_workspace_bytes_for(lib):
                                                 (2, 4, 2, 300, 700, 64, 50, 1),
                                                 (1, 64, 8, 4096, 4096, 128, 0, 4),
                                                 (1, 64, 8, 4096, 4096, 128, 256, 0),
-                                                (1, 4, 2, 640, 640, 128, 70, 130)):
+                                                (1, 4, 2, 640, 640, 128, 70, 130),
+                                                (1, 64, 8, 8192, 8192, 64, 1024, 4),
+                                                (1, 8, 2, 2048, 2048, 64, 128, 4)):
         base = fa.attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
-        nc = _sink_chunks(B, Hq, Hkv, Sq, Sk, window, sink)
+        nc = _sink_chunks(B, Hq, Hkv, Sq, Sk, D, window, sink)
         extra = 2 * nc * _parts(B, Hq, Hkv, Sk) * B * Hkv * 128 * D * 4 if nc > 1 else 0
         got = fa.attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, True, window, sink)
         assert got == base + extra, (B, Hq, Hkv, Sq, Sk, D, window, sink, nc)
     # the sliding-window workload with 4 sinks: tile 0 is seen by all 128 query tiles, any other
     # tile by 18, so 26 chunks of 5; with 16 batch rows the ordinary work outweighs tile 0: no split
-    assert _sink_chunks(1, 64, 8, 8192, 8192, 1024, 4) == 26
+    assert _sink_chunks(1, 64, 8, 8192, 8192, 128, 1024, 4) == 26
     assert fa.attn_bwd_qk_workspace_bytes_for(1, 64, 8, 8192, 8192, 128, True, 1024, 4) == \
         fa.attn_bwd_qk_workspace_bytes(1, 64, 8, 8192, 8192, 128) + 2 * 26 * 8 * 128 * 128 * 4
-    assert _sink_chunks(16, 64, 8, 8192, 8192, 1024, 4) == 1
+    assert _sink_chunks(16, 64, 8, 8192, 8192, 128, 1024, 4) == 1
     assert fa.attn_bwd_qk_workspace_bytes_for(16, 64, 8, 8192, 8192, 128, True, 1024, 4) == \
         fa.attn_bwd_qk_workspace_bytes(16, 64, 8, 8192, 8192, 128)
     assert fa.attn_bwd_qk_workspace_bytes_for(1, 2, 2, 65, 64, 64, True, 8, 1) == 0  # rejected

@@ -137,9 +137,11 @@ def test_sink_workload_full_size_sampled():
 
 SPLIT_CASES = [
     # B, Hq, Hkv, S, D, window, sink: head group split in 4 / two batch rows / S not a multiple of 128
+    # (D = 64 streams 128-row query tiles, D = 128 64-row tiles)
     (1, 8, 2, 1024, 128, 128, 4),
     (2, 4, 2, 768, 64, 64, 2),
     (1, 4, 4, 600, 128, 100, 1),
+    (1, 4, 2, 1000, 64, 96, 3),
 ]
 
 
