@@ -38,6 +38,14 @@ __device__ __forceinline__ void dma_tile_wave(char* lds, RowPtr rowptr, int row0
   }
 }
 
+// Chunk c (keys [c * kDecChunk, c * kDecChunk + kDecChunk)) holds no key that a query of the
+// sequence (positions off .. off + Sq - 1 of S keys) sees.
+__device__ __forceinline__ bool decode_chunk_empty(int c, int off, int Sq, int S, int causal, int window,
+                                                   int sink) {
+  const int c0 = c * kDecChunk;
+  return c0 >= S || block_empty(off, off + Sq - 1, c0, c0 + kDecChunk - 1, S, causal, window, sink);
+}
+
 // part layout per (chunk, b, g): R rows x D floats of unnormalised O, then R maxima (base 2), then
 // R sums.
 __device__ __forceinline__ size_t dec_part_index(int chunk, int bg, int BG, int R, int D) {
@@ -74,6 +82,9 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(
 
   if constexpr (PG) S = imin_(imax_(pg.seqlen[b], Sq), pg.max_blocks << pg.shift);
   const int off = S - Sq;
+  // A chunk past this sequence's keys or outside every query's window holds nothing: the whole
+  // workgroup leaves at once and the combine skips the chunk by the same test.
+  if (decode_chunk_empty(chunk, off, Sq, S, causal, window, sink)) return;
 
   // This lane's packed row: query head g*G + hh, query i at position off + i.
   const int n = l32;
@@ -182,11 +193,14 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(
   }
 }
 
-// One workgroup of D threads per (b, g, packed row): merge the chunks in chunk order.
-template <int D>
+// One workgroup of D threads per (b, g, packed row): merge the non-empty chunks in chunk order.
+// The chunk holding the row's own position is never empty, so L > 0. The loads stay unconditional
+// (so they can be issued ahead): an empty chunk reads that chunk's partial instead and weighs 0.
+template <int D, bool PG>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part,
                                                              uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                                             int B, int Hq, int Hkv, int Sq, int n_chunk) {
+                                                             int B, int Hq, int Hkv, int Sq, int S, int causal,
+                                                             int window, int sink, int n_chunk, PagedKV pg) {
   const int G = Hq / Hkv;
   const int R = G * Sq;
   const int BG = B * Hkv;
@@ -195,13 +209,23 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
   const int d = threadIdx.x;
-  float M = kNegInf;
-  for (int c = 0; c < n_chunk; ++c) M = fmaxf(M, part[dec_part_index(c, bg, BG, R, D) + R * D + row]);
+  if constexpr (PG) S = imin_(imax_(pg.seqlen[b], Sq), pg.max_blocks << pg.shift);
+  const int off = S - Sq;
+  const int nc = imin_(n_chunk, (S + kDecChunk - 1) / kDecChunk);  // later chunks lie past the keys
+  const int c_self = (off + row % Sq) / kDecChunk;
+  float M = kNegInf;  // a duplicate of chunk c_self leaves the maximum unchanged
+#pragma unroll 8
+  for (int c = 0; c < nc; ++c) {
+    const int cc = decode_chunk_empty(c, off, Sq, S, causal, window, sink) ? c_self : c;
+    M = fmaxf(M, part[dec_part_index(cc, bg, BG, R, D) + R * D + row]);
+  }
   float o = 0.f, L = 0.f;
-  for (int c = 0; c < n_chunk; ++c) {
-    const float* p = part + dec_part_index(c, bg, BG, R, D);
+#pragma unroll 8
+  for (int c = 0; c < nc; ++c) {
+    const bool e = decode_chunk_empty(c, off, Sq, S, causal, window, sink);
+    const float* p = part + dec_part_index(e ? c_self : c, bg, BG, R, D);
     const float mc = p[R * D + row];
-    const float f = mc == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+    const float f = (e || mc == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
     o += f * p[row * D + d];
     L += f * p[R * D + R + row];
   }
@@ -233,8 +257,9 @@ static int launch_decode_t(const Args& a, float* part, int max_keys) {
                      a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, scale_log2, n_chunk, a.pg);
   notify_launch("attn_decode", 1, a.stream);
   notify_launch("attn_decode_combine", 0, a.stream);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(BG * R)), dim3(D), 0, st,
-                     (const float*)part, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, n_chunk);
+  auto comb = a.paged ? decode_combine_kernel<D, true> : decode_combine_kernel<D, false>;
+  hipLaunchKernelGGL(comb, dim3((unsigned)(BG * R)), dim3(D), 0, st, (const float*)part, (uint16_t*)a.o,
+                     a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, n_chunk, a.pg);
   notify_launch("attn_decode_combine", 1, a.stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

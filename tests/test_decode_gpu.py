@@ -86,9 +86,12 @@ def test_decode_matches_tiled_forward_and_is_deterministic():
     assert np.max(np.abs(L1 - lse.double().cpu().numpy())) <= 1e-3
 
 
-@pytest.mark.parametrize("bs,Sq", [(16, 1), (64, 2), (256, 1)])
-def test_decode_paged_parity(bs, Sq):
-    say(f"decode paged bs={bs} Sq={Sq}")
+@pytest.mark.parametrize("bs,Sq,window,sink", [(16, 1, 0, 0), (64, 2, 0, 0), (256, 1, 0, 0), (16, 1, 300, 3),
+                                               (32, 3, 1000, 0)])
+def test_decode_paged_parity(bs, Sq, window, sink):
+    """Sequences of 1500, 70, 4100 and 129 keys: the longer ones leave chunks that lie past the
+    shorter ones' keys or (with a window) before every query's window; those chunks are skipped."""
+    say(f"decode paged bs={bs} Sq={Sq} window={window} sink={sink}")
     dtype, Hq, Hkv, D = "bf16", 32, 4, 128
     lens = [1500, 70, 4100, 129]
     B, Smax = len(lens), max(lens)
@@ -111,9 +114,10 @@ def test_decode_paged_parity(bs, Sq):
             n = min(bs, lens[b] - t * bs)
             kp[ph, :, :n] = kd[b, :, t * bs:t * bs + n]
             vp[ph, :, :n] = vd[b, :, t * bs:t * bs + n]
-    O, L = _decode(q, kp, vp, dtype, table=table, lens=lens, max_keys=table.shape[1] * bs)
-    ref_o, ref_l = oracle.paged_forward(q, kp.astype(np.float64), vp.astype(np.float64), table, lens, True, 0,
-                                        1.0 / math.sqrt(D))
+    scale = 1.0 / math.sqrt(D)
+    O, L = _decode(q, kp, vp, dtype, window, sink, scale, table=table, lens=lens, max_keys=table.shape[1] * bs)
+    ref_o, ref_l = oracle.paged_forward(q, kp.astype(np.float64), vp.astype(np.float64), table, lens, True,
+                                        window, scale, sink=sink)
     eo, el = oracle.rel_l2(O, ref_o), oracle.rel_l2(L, ref_l)
     say(f"  parity O={eo:.2e} LSE={el:.2e}")
     assert eo <= GATES[dtype]["O"] and el <= GATES[dtype]["LSE"]
