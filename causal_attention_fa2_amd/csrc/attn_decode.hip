@@ -193,9 +193,11 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(
   }
 }
 
-// One workgroup of D threads per (b, g, packed row): merge the non-empty chunks in chunk order.
-// The chunk holding the row's own position is never empty, so L > 0. The loads stay unconditional
-// (so they can be issued ahead): an empty chunk reads that chunk's partial instead and weighs 0.
+// One workgroup of D threads per (b, g, packed row): merge the non-empty chunks in chunk order, one
+// pass over groups of kCombGroup chunks with a running maximum (all of a group's loads are issued
+// before any is used). The chunk holding the row's own position is never empty, so L > 0. The
+// loads stay unconditional: an empty chunk reads that chunk's partial instead and weighs 0.
+constexpr int kCombGroup = 16;
 template <int D, bool PG>
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ part,
                                                              uint16_t* __restrict__ O, float* __restrict__ LSE,
@@ -213,21 +215,34 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
   const int off = S - Sq;
   const int nc = imin_(n_chunk, (S + kDecChunk - 1) / kDecChunk);  // later chunks lie past the keys
   const int c_self = (off + row % Sq) / kDecChunk;
-  float M = kNegInf;  // a duplicate of chunk c_self leaves the maximum unchanged
-#pragma unroll 8
-  for (int c = 0; c < nc; ++c) {
-    const int cc = decode_chunk_empty(c, off, Sq, S, causal, window, sink) ? c_self : c;
-    M = fmaxf(M, part[dec_part_index(cc, bg, BG, R, D) + R * D + row]);
-  }
-  float o = 0.f, L = 0.f;
-#pragma unroll 8
-  for (int c = 0; c < nc; ++c) {
-    const bool e = decode_chunk_empty(c, off, Sq, S, causal, window, sink);
-    const float* p = part + dec_part_index(e ? c_self : c, bg, BG, R, D);
-    const float mc = p[R * D + row];
-    const float f = (e || mc == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-    o += f * p[row * D + d];
-    L += f * p[R * D + R + row];
+  float M = kNegInf, o = 0.f, L = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += kCombGroup) {
+    float mc[kCombGroup], oc[kCombGroup], lc[kCombGroup];
+#pragma unroll
+    for (int u = 0; u < kCombGroup; ++u) {
+      const int c = c0 + u;
+      const bool use = c < nc && !decode_chunk_empty(c, off, Sq, S, causal, window, sink);
+      const float* p = part + dec_part_index(use ? c : c_self, bg, BG, R, D);
+      mc[u] = p[R * D + row];
+      oc[u] = p[row * D + d];
+      lc[u] = p[R * D + R + row];
+      if (!use) mc[u] = kNegInf;
+    }
+    float gm = M;
+#pragma unroll
+    for (int u = 0; u < kCombGroup; ++u) gm = fmaxf(gm, mc[u]);
+    if (gm != kNegInf) {
+      const float r = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - gm);
+      o *= r;
+      L *= r;
+#pragma unroll
+      for (int u = 0; u < kCombGroup; ++u) {
+        const float f = mc[u] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mc[u] - gm);
+        o += f * oc[u];
+        L += f * lc[u];
+      }
+      M = gm;
+    }
   }
   const int hh = row / Sq;
   const int qi = row - hh * Sq;
