@@ -28,7 +28,7 @@
 namespace fa {
 
 template <class E, int D, int NW, int KB, bool VL>
-__global__ __launch_bounds__(NW * 64) void dq_kernel(
+__global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const typename E::T* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ LSE2,
@@ -207,24 +207,35 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   }
 }
 
+// Key tiles: bf16 with 8 waves 64 keys (128 for D = 64: 3% faster); bf16 with 4 waves 32 keys (64
+// for D = 64), so that the three-stage ring takes at most 56 KB of LDS and two workgroups share a
+// compute unit; fp32 32 keys.
+template <class E, int D, int NW, bool VL>
+static void launch_dq_nw(const Args& a) {
+  typedef typename E::T T;
+  constexpr int KB = E::kBytes == 2 ? (NW == 4 ? (D == 64 ? 2 : 1) : (D == 64 ? 4 : 2)) : 1;
+  const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+  const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
+  hipLaunchKernelGGL((dq_kernel<E, D, NW, KB, VL>), dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(NW * 64), 0,
+                     (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+                     (const T*)a.o_in, (const float*)a.lse, a.lse2, a.delta, (T*)a.dq, a.B, a.Hq, a.Hkv, a.Sq,
+                     a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt, a.docs);
+}
+
+// Waves per workgroup as in the forward: 8 (bf16; kWinWaves / kDocWaves for a sliding window /
+// packed documents) or 4 (fp32).
 template <class E, int D>
 static int launch_bwd_t(const Args& a) {
-  hipStream_t st = (hipStream_t)a.stream;
-  typedef typename E::T T;
-  const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-  {
-    constexpr int NW = E::kBytes == 2 ? 8 : 4;
-    constexpr int KB = E::kBytes == 2 ? (D == 64 ? 4 : 2) : 1;  // 128-key tiles for D = 64 (3% faster)
-    const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
-    dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
-    notify_launch("attn_bwd_dq", 0, a.stream);
-    auto kern = a.docs.cu ? dq_kernel<E, D, NW, KB, true> : dq_kernel<E, D, NW, KB, false>;
-    hipLaunchKernelGGL(kern, grid, block, 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                       (const T*)a.dout, (const T*)a.o_in, (const float*)a.lse, a.lse2, a.delta, (T*)a.dq,
-                       a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt,
-                       a.docs);
-    notify_launch("attn_bwd_dq", 1, a.stream);
+  notify_launch("attn_bwd_dq", 0, a.stream);
+  if constexpr (E::kBytes == 2) {
+    if (a.docs.cu) launch_dq_nw<E, D, kDocWaves, true>(a);
+    else if (a.window > 0) launch_dq_nw<E, D, kWinWaves, false>(a);
+    else launch_dq_nw<E, D, 8, false>(a);
+  } else {
+    if (a.docs.cu) launch_dq_nw<E, D, 4, true>(a);
+    else launch_dq_nw<E, D, 4, false>(a);
   }
+  notify_launch("attn_bwd_dq", 1, a.stream);
   // the dK / dV pass reads the delta and base-2 log-sum-exp rows that dq_kernel stored
   if (launch_dkdv(a) != 0) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -241,23 +241,36 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
 // S = 4096 and no different on the S_q = 1024 / 1 shapes), f32 three. Key tiles: 64 keys, 128 for
 // bf16 with D = 64 (half the products per key block, so a longer tile per step: 12% faster there);
 // the paged copy takes at most 64 rows per tile.
-template <class E, int D>
-static int launch_fwd_t(const Args& a) {
-  constexpr int NW = E::kBytes == 2 ? kFwdWaves : 4;
-  constexpr int KB = E::kBytes == 2 ? (D == 64 ? 4 : 2) : 1;
-  constexpr int KBP = E::kBytes == 2 ? 2 : 1;  // paged: tiles of at most 64 rows
+template <class E, int D, int NW, bool PG, bool VL>
+static void launch_fwd_nw(const Args& a) {
+  constexpr int KB = E::kBytes == 2 ? (PG ? 2 : (D == 64 ? 4 : 2)) : 1;  // paged: tiles of at most 64 rows
   constexpr int NST = E::kBytes == 2 ? kFwdStages : 3;
   const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
-  dim3 grid((unsigned)(n_qt * a.B * a.Hq)), block(NW * 64);
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NST, PG, VL>), dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(NW * 64),
+                     0, (hipStream_t)a.stream, (const typename E::T*)a.q, (const typename E::T*)a.k,
+                     (const typename E::T*)a.v, (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
+                     a.causal, a.window, a.sink, scale_log2, n_qt, a.pg, a.docs);
+}
+
+// Ring depth: bf16 two stages (one tile in flight; measured about 1% faster than three at
+// S = 4096 and no different on the S_q = 1024 / 1 shapes), f32 three. Key tiles: 64 keys, 128 for
+// bf16 with D = 64 (half the products per key block, so a longer tile per step: 12% faster there);
+// the paged copy takes at most 64 rows per tile. Waves: kFwdWaves, or kWinWaves / kDocWaves for
+// the short key ranges of a sliding window / packed documents.
+template <class E, int D>
+static int launch_fwd_t(const Args& a) {
   notify_launch("attn_fwd", 0, a.stream);
-  auto kern = a.paged ? fwd_kernel<E, D, NW, KBP, NST, true, false>
-                       : (a.docs.cu ? fwd_kernel<E, D, NW, KB, NST, false, true>
-                                    : fwd_kernel<E, D, NW, KB, NST, false, false>);
-  hipLaunchKernelGGL(kern, grid, block, 0, (hipStream_t)a.stream, (const typename E::T*)a.q,
-                     (const typename E::T*)a.k, (const typename E::T*)a.v, (typename E::T*)a.o, a.lse,
-                     a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink, scale_log2, n_qt, a.pg,
-                     a.docs);
+  if constexpr (E::kBytes == 2) {
+    if (a.paged) launch_fwd_nw<E, D, kFwdWaves, true, false>(a);
+    else if (a.docs.cu) launch_fwd_nw<E, D, kDocWaves, false, true>(a);
+    else if (a.window > 0) launch_fwd_nw<E, D, kWinWaves, false, false>(a);
+    else launch_fwd_nw<E, D, kFwdWaves, false, false>(a);
+  } else {
+    if (a.paged) launch_fwd_nw<E, D, 4, true, false>(a);
+    else if (a.docs.cu) launch_fwd_nw<E, D, 4, false, true>(a);
+    else launch_fwd_nw<E, D, 4, false, false>(a);
+  }
   notify_launch("attn_fwd", 1, a.stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

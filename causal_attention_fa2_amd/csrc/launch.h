@@ -75,6 +75,17 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int max_keys, int 
 #define ATTN_FWD_STAGES 2
 #endif
 constexpr int kFwdWaves = ATTN_FWD_WAVES, kFwdStages = ATTN_FWD_STAGES;
+// Waves per workgroup of the bf16 forward and dQ passes when the visible key range of a row is short
+// (a sliding window, packed documents): a workgroup walks the union of its waves' key ranges, which
+// for 32*NW rows exceeds one wave's by up to 32*(NW-1) keys. 4 waves: forward 6-15% and dQ 9-15%
+// faster than 8 on the window, window + sinks and packed-document workloads.
+#ifndef ATTN_WIN_WAVES
+#define ATTN_WIN_WAVES 4
+#endif
+#ifndef ATTN_DOC_WAVES
+#define ATTN_DOC_WAVES 4
+#endif
+constexpr int kWinWaves = ATTN_WIN_WAVES, kDocWaves = ATTN_DOC_WAVES;
 
 // dK/dV decomposition: a workgroup of kDkdvWaves waves owns 32*kDkdvWaves keys and processes key
 // tile j and then key tile n_kt-1-j (equal work per workgroup under the causal mask). When that

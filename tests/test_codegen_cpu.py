@@ -33,4 +33,5 @@ def test_forward_dot2_reads_distinct_words(tmp_path):
         for i in range(0, len(srcs), 4):
             assert len(set(srcs[i:i + 4])) == 4, (k[:60], srcs[i:i + 4])
         checked += 1
-    assert checked == 6  # bf16 D=64 and D=128: dense, paged K/V, packed documents
+    # bf16 D=64 and D=128: dense (8 waves), sliding window (4 waves), paged K/V, packed documents
+    assert checked == 8
