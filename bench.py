@@ -222,7 +222,8 @@ def bench_paged(w, args, torch, fa) -> int:
                    "path": "attn_decode_fwd" if w.decode else "attn_fwd_paged",
                    "window": w.window, "parallelism": "none (1 GPU)"},
         "kernel_ms_median": round(kmed, 4),
-        "roofline": {"kernel": "attn_fwd", "bound": "hbm" if Sq * (w.Hq // w.Hkv) <= 64 else "mfma",
+        "roofline": {"kernel": "attn_decode + attn_decode_combine" if w.decode else "attn_fwd",
+                     "bound": "hbm" if Sq * (w.Hq // w.Hkv) <= 64 else "mfma",
                      "achieved": round(gbs, 1) if Sq * (w.Hq // w.Hkv) <= 64 else
                      round(flops / (kmed * 1e-3) / 1e12, 1),
                      "peak": PEAK_HBM_GBS if Sq * (w.Hq // w.Hkv) <= 64 else PEAK_BF16_TFLOPS,
