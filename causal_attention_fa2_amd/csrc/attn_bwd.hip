@@ -222,14 +222,13 @@ static void launch_dq_nw(const Args& a) {
                      a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt, a.docs);
 }
 
-// Waves per workgroup as in the forward: 8 (bf16; kWinWaves / kDocWaves for a sliding window /
-// packed documents) or 4 (fp32).
+// Waves per workgroup as in the forward: 8 (bf16; kShortWaves for short key ranges) or 4 (fp32).
 template <class E, int D>
 static int launch_bwd_t(const Args& a) {
   notify_launch("attn_bwd_dq", 0, a.stream);
   if constexpr (E::kBytes == 2) {
-    if (a.docs.cu) launch_dq_nw<E, D, kDocWaves, true>(a);
-    else if (a.window > 0) launch_dq_nw<E, D, kWinWaves, false>(a);
+    if (a.docs.cu) launch_dq_nw<E, D, kShortWaves, true>(a);
+    else if (short_key_ranges(a)) launch_dq_nw<E, D, kShortWaves, false>(a);
     else launch_dq_nw<E, D, 8, false>(a);
   } else {
     if (a.docs.cu) launch_dq_nw<E, D, 4, true>(a);

@@ -256,15 +256,15 @@ static void launch_fwd_nw(const Args& a) {
 // Ring depth: bf16 two stages (one tile in flight; measured about 1% faster than three at
 // S = 4096 and no different on the S_q = 1024 / 1 shapes), f32 three. Key tiles: 64 keys, 128 for
 // bf16 with D = 64 (half the products per key block, so a longer tile per step: 12% faster there);
-// the paged copy takes at most 64 rows per tile. Waves: kFwdWaves, or kWinWaves / kDocWaves for
-// the short key ranges of a sliding window / packed documents.
+// the paged copy takes at most 64 rows per tile. Waves: kFwdWaves, or kShortWaves for short key
+// ranges (short_key_ranges).
 template <class E, int D>
 static int launch_fwd_t(const Args& a) {
   notify_launch("attn_fwd", 0, a.stream);
   if constexpr (E::kBytes == 2) {
     if (a.paged) launch_fwd_nw<E, D, kFwdWaves, true, false>(a);
-    else if (a.docs.cu) launch_fwd_nw<E, D, kDocWaves, false, true>(a);
-    else if (a.window > 0) launch_fwd_nw<E, D, kWinWaves, false, false>(a);
+    else if (a.docs.cu) launch_fwd_nw<E, D, kShortWaves, false, true>(a);
+    else if (short_key_ranges(a)) launch_fwd_nw<E, D, kShortWaves, false, false>(a);
     else launch_fwd_nw<E, D, kFwdWaves, false, false>(a);
   } else {
     if (a.paged) launch_fwd_nw<E, D, 4, true, false>(a);

@@ -75,17 +75,27 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int max_keys, int 
 #define ATTN_FWD_STAGES 2
 #endif
 constexpr int kFwdWaves = ATTN_FWD_WAVES, kFwdStages = ATTN_FWD_STAGES;
-// Waves per workgroup of the bf16 forward and dQ passes when the visible key range of a row is short
-// (a sliding window, packed documents): a workgroup walks the union of its waves' key ranges, which
-// for 32*NW rows exceeds one wave's by up to 32*(NW-1) keys. 4 waves: forward 6-15% and dQ 9-15%
-// faster than 8 on the window, window + sinks and packed-document workloads.
-#ifndef ATTN_WIN_WAVES
-#define ATTN_WIN_WAVES 4
+// Waves per workgroup of the bf16 forward and dQ passes when the visible key range of a row is short:
+// a workgroup walks the union of its waves' key ranges, which for 32*NW rows exceeds one wave's by
+// up to 32*(NW-1) keys. Measured against 8 waves: forward 6-15% and dQ 9-15% faster on the
+// sliding-window (W = 1024) and packed-document (1.1-1.7k-token) workloads and on dense causal
+// S = 1024; dense causal S = 4096 (2k keys per row on average) is 1.5% slower.
+#ifndef ATTN_SHORT_WAVES
+#define ATTN_SHORT_WAVES 4
 #endif
-#ifndef ATTN_DOC_WAVES
-#define ATTN_DOC_WAVES 4
+#ifndef ATTN_SHORT_KEYS
+#define ATTN_SHORT_KEYS 1024
 #endif
-constexpr int kWinWaves = ATTN_WIN_WAVES, kDocWaves = ATTN_DOC_WAVES;
+constexpr int kShortWaves = ATTN_SHORT_WAVES, kShortKeys = ATTN_SHORT_KEYS;
+// Short key ranges (the waves of a 32*kFwdWaves-row workgroup would idle much of the time): packed
+// documents, or at most kShortKeys keys per query row on average (queries at the last Sq positions:
+// a causal row at position p sees p + 1 keys, at most `window`).
+inline bool short_key_ranges(const Args& a) {
+  if (a.docs.cu) return true;
+  double mean = a.causal ? (a.Sk - a.Sq) + (a.Sq + 1) / 2.0 : (double)a.Sk;
+  if (a.window > 0 && mean > a.window) mean = a.window;
+  return mean <= kShortKeys;
+}
 
 // dK/dV decomposition: a workgroup of kDkdvWaves waves owns 32*kDkdvWaves keys and processes key
 // tile j and then key tile n_kt-1-j (equal work per workgroup under the causal mask). When that
