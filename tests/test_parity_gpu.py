@@ -35,6 +35,12 @@ SMALL_CASES = [
     ("bf16", 1, 4, 2, 385, 64, True, 65),
     ("bf16", 1, 2, 2, 500, 128, True, 200),
     ("bf16", 1, 2, 1, 190, 128, False, 0),
+    # more than 1024 visible keys per row on average: the 8-wave (256-row) forward and dQ workgroups
+    # (the cases above run the 4-wave ones)
+    ("bf16", 1, 4, 2, 2200, 128, True, 0),
+    ("bf16", 1, 2, 2, 2113, 64, True, 0),
+    ("bf16", 1, 2, 1, 2600, 128, True, 1500),
+    ("bf16", 1, 2, 2, 1100, 64, False, 0),
 ]
 
 
