@@ -125,6 +125,30 @@ def host_info():
     return model, blas
 
 
+def cpu_sample(w, heads: int, cu=None):
+    """(query heads, KV groups, query rows, attended pairs per head) of the CPU-oracle sample: the
+    first `heads` query heads as whole KV groups; without documents it is then kept to about
+    CPU_SAMPLE_PAIRS attended pairs (10-30 s of oracle work) by taking one KV group, then one query
+    head, then the last query rows (the oracle takes S_q <= S_k)."""
+    G = w.Hq // w.Hkv
+    heads = max(G, min(w.Hq, heads // G * G))
+    groups = heads // G
+    rows = w.n_q
+    if cu is not None:
+        pairs = sum(attended_pairs(int(b - a), True, w.window) for row in cu
+                    for a, b in zip(row[:-1], row[1:]) if b > a) / w.B
+        return heads, groups, rows, pairs
+    pairs = attended_pairs(w.S, w.causal, w.window, rows, w.sink)
+    if w.B * heads * pairs > CPU_SAMPLE_PAIRS:
+        heads, groups = G, 1
+    if w.B * heads * pairs > CPU_SAMPLE_PAIRS:
+        heads = 1
+    while rows > 64 and w.B * heads * pairs > CPU_SAMPLE_PAIRS:
+        rows //= 2
+        pairs = attended_pairs(w.S, w.causal, w.window, rows, w.sink)
+    return heads, groups, rows, pairs
+
+
 def cpu_baseline(w, q, k, v, do, heads: int):
     """The fp64 oracle, timed on this host's cores, on the first `heads` query heads (whole KV
     groups) of the same inputs."""
@@ -134,27 +158,11 @@ def cpu_baseline(w, q, k, v, do, heads: int):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # threadpoolctl missing: report the affinity mask instead
         threads = len(os.sched_getaffinity(0))
-    G = w.Hq // w.Hkv
-    heads = max(G, min(w.Hq, heads // G * G))
-    groups = heads // G
-    rows = w.n_q
     cu = None
-    pairs = attended_pairs(w.S, w.causal, w.window, rows, w.sink)
     if w.docs:
         from causal_attention_fa2_amd.workloads import document_boundaries
         cu = document_boundaries(w)
-        pairs = sum(attended_pairs(int(b - a), True, w.window) for row in cu
-                    for a, b in zip(row[:-1], row[1:]) if b > a) / w.B
-    else:
-        # keep the sample to about CPU_SAMPLE_PAIRS attended pairs (10-30 s of oracle work): one KV
-        # group, then one query head, then the last `rows` query rows (the oracle takes S_q <= S_k)
-        if w.B * heads * pairs > CPU_SAMPLE_PAIRS:
-            heads, groups = G, 1
-        if w.B * heads * pairs > CPU_SAMPLE_PAIRS:
-            heads = 1
-        while rows > 64 and w.B * heads * pairs > CPU_SAMPLE_PAIRS:
-            rows //= 2
-            pairs = attended_pairs(w.S, w.causal, w.window, rows, w.sink)
+    heads, groups, rows, pairs = cpu_sample(w, heads, cu)
     r0 = w.n_q - rows
     t0 = time.perf_counter()
     oracle.forward_backward(q[:, :heads, r0:], k[:, :groups], v[:, :groups], do[:, :heads, r0:],

@@ -21,3 +21,24 @@ def test_attended_pairs(S, Sq, causal, window, sink):
         assert got == exact - Sq / 2.0
     else:
         assert got == exact
+
+
+def test_cpu_sample_is_bounded():
+    """The CPU-oracle sample keeps whole KV groups while it fits, then one group, one head and
+    finally the last query rows, never above bench.CPU_SAMPLE_PAIRS attended pairs (documents aside)."""
+    from causal_attention_fa2_amd.workloads import WORKLOADS
+    # the S = 4096 headline: all 64 heads, every row (5.4e8 pairs)
+    assert bench.cpu_sample(WORKLOADS["gqa64x8-s4096-d128"], 64)[:3] == (64, 8, 4096)
+    # S = 32768: one query head of the first KV group, every row
+    h, g, rows, pairs = bench.cpu_sample(WORKLOADS["gqa64x8-s32768-d128"], 64)
+    assert (h, g, rows) == (1, 1, 32768) and pairs == 32768 * 32768 / 2  # S^2/2, the FLOP convention
+    # whole groups are kept when they fit; --cpu-heads rounds to whole groups
+    assert bench.cpu_sample(WORKLOADS["small-mha-causal-bf16"], 64)[:3] == (16, 16, 1024)
+    assert bench.cpu_sample(WORKLOADS["gqa64x8-s4096-d128"], 20)[:3] == (16, 2, 4096)
+    for name, w in WORKLOADS.items():
+        if w.docs or w.paged or w.decode:
+            continue
+        h, g, rows, pairs = bench.cpu_sample(w, 64)
+        assert 1 <= rows <= w.n_q and 1 <= h <= w.Hq and 1 <= g <= w.Hkv, name
+        assert w.B * h * pairs <= bench.CPU_SAMPLE_PAIRS or rows <= 64, name
+        assert pairs == bench.attended_pairs(w.S, w.causal, w.window, rows, w.sink), name
