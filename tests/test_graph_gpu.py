@@ -4,7 +4,8 @@ with the outputs overwritten by eager work between replays, and every replay mus
 eager call bit for bit (the kernels sum in a fixed order, so reruns are bitwise equal).
 
 Covered: forward + backward with the head-split reduce, the backward with the sink split and its
-chunk reduce, and the key-split decode forward with its combine."""
+chunk reduce, and the key-split decode forward with its combine. A last test runs two problems at
+once on two streams."""
 import math
 
 import numpy as np
@@ -140,3 +141,45 @@ def test_graph_decode_paged():
     want = [o.clone(), lse.clone()]
     g = _capture(step)
     _replay_and_check(g, [o, lse], want, "paged decode")
+
+
+def test_two_streams_concurrently():
+    """Two different problems enqueued at once on two non-default streams (each with its own
+    workspace): the library keeps no per-call state, so each result equals the same call made
+    alone, bit for bit."""
+    import torch
+    import causal_attention_fa2_amd as fa
+    fa.attn_set_launch_hook(None)
+    say("two streams")
+    cases = [(1, 8, 2, 1000, 128, 0, 330), (2, 4, 4, 700, 64, 200, 340)]
+    bufs = []
+    for B, Hq, Hkv, S, D, W, seed in cases:
+        q, k, v, do = _inputs("bf16", B, Hq, Hkv, S, S, D, seed)
+        ws = torch.empty(fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D), dtype=torch.uint8, device="cuda")
+        outs = (torch.empty_like(q), torch.empty((B, Hq, S), dtype=torch.float32, device="cuda"),
+                torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        bufs.append((q, k, v, do, ws, outs, W, 1.0 / math.sqrt(D)))
+
+    def run(buf, stream):
+        q, k, v, do, ws, (o, lse, dq, dk, dv), W, scale = buf
+        fa.attn_fwd(q, k, v, o, lse, True, W, scale, stream)
+        fa.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, True, W, scale, stream)
+
+    want = []
+    for buf in bufs:  # alone, one after the other
+        run(buf, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        want.append([t.clone() for t in buf[5]])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for buf in bufs:
+            for t in buf[5]:
+                t.fill_(7)
+        torch.cuda.synchronize()
+        for buf, st in zip(bufs, streams):
+            run(buf, st)
+        torch.cuda.synchronize()
+        for i, buf in enumerate(bufs):
+            for got, ref in zip(buf[5], want[i]):
+                assert torch.equal(got, ref), f"case {i}, repetition {rep}"
+    say("  two streams: results equal to the serial calls")
