@@ -48,14 +48,20 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     """Compile every HIP source (each with its own flags) and link libattn.so next to this file;
     returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
     out_dir = os.path.join(ROOT, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    objs = []
+    jobs = []
     for src, extra in SOURCES:
         obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
-        _run([hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
-              os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append((obj, [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
+                           os.path.join(CSRC, src), "-o", obj]))
+    # the sources compile independently: one hipcc per source, in parallel
+    workers = max(1, min(len(jobs), os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for _, cmd in jobs]:
+            f.result()
+    objs = [obj for obj, _ in jobs]
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
