@@ -88,11 +88,13 @@ constexpr int kFwdWaves = ATTN_FWD_WAVES, kFwdStages = ATTN_FWD_STAGES;
 #endif
 constexpr int kShortWaves = ATTN_SHORT_WAVES, kShortKeys = ATTN_SHORT_KEYS;
 // Short key ranges (the waves of a 32*kFwdWaves-row workgroup would idle much of the time): packed
-// documents, or at most kShortKeys keys per query row on average (queries at the last Sq positions:
-// a causal row at position p sees p + 1 keys, at most `window`).
+// documents, or at most kShortKeys keys per query row on average over the whole sequence (a causal
+// row at position p sees p + 1 keys, at most `window`). The test looks at Sk, causal and window
+// only, never at Sq, so a query chunk (Sq < Sk) runs the same workgroups, and gives the same bits,
+// as its rows do in the call over all Sk queries.
 inline bool short_key_ranges(const Args& a) {
   if (a.docs.cu) return true;
-  double mean = a.causal ? (a.Sk - a.Sq) + (a.Sq + 1) / 2.0 : (double)a.Sk;
+  double mean = a.causal ? (a.Sk + 1) / 2.0 : (double)a.Sk;
   if (a.window > 0 && mean > a.window) mean = a.window;
   return mean <= kShortKeys;
 }

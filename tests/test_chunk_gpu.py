@@ -71,6 +71,10 @@ def test_chunk_small_parity(case):
     ("bf16", 4, 2, 100, 450, 64, 0),     # ragged: not on a tile boundary
     ("bf16", 4, 2, 256, 1024, 128, 200),
     ("bf16", 8, 2, 1, 700, 128, 0),
+    # S_k = 2000: the rows' mean key count (1000) picks 4-wave workgroups; the chunk alone would
+    # average 1950 keys per row, so the choice must not look at S_q
+    ("bf16", 4, 2, 100, 2000, 128, 0),
+    ("bf16", 4, 2, 1, 2000, 64, 0),
     ("f32", 2, 2, 96, 320, 64, 0),
     ("f32", 2, 1, 50, 260, 128, 70),
 ])
@@ -95,7 +99,7 @@ def test_chunk_is_bitwise_slice_of_square(dtype, Hq, Hkv, Sq, Sk, D, window):
     assert torch.equal(o_c, o_f[:, :, off:]), "O"
     assert torch.equal(l_c, l_f[:, :, off:]), "lse"
     assert torch.equal(dq_c, dq_f[:, :, off:]), "dQ"
-    br = 64 if dtype == "bf16" else 32  # query rows per tile of the dK/dV pass
+    br = (128 if D == 64 else 64) if dtype == "bf16" else 32  # query rows per tile of the dK/dV pass
     if off % br == 0:
         assert torch.equal(dk_c, dk_f) and torch.equal(dv_c, dv_f), "dK / dV"
     else:

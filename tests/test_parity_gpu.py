@@ -41,6 +41,10 @@ SMALL_CASES = [
     ("bf16", 1, 2, 2, 2113, 64, True, 0),
     ("bf16", 1, 2, 1, 2600, 128, True, 1500),
     ("bf16", 1, 2, 2, 1100, 64, False, 0),
+    # D = 64 dK/dV streams 128-row query tiles: windows and lengths either side of 128
+    ("bf16", 1, 4, 2, 643, 64, True, 127),
+    ("bf16", 2, 8, 2, 515, 64, True, 129),
+    ("bf16", 1, 4, 1, 257, 64, True, 128),
 ]
 
 
