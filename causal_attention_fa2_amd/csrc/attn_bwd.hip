@@ -42,9 +42,9 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
   typedef LdsTile<E, BC, D> KvTile;
   constexpr int kStage = 2 * KvTile::kBytes;
   constexpr int kOps = 2 * dma_tile_ops<E, BC, D, NW>();
-  __shared__ __attribute__((aligned(1024))) char st0[kStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kStage];
-  __shared__ __attribute__((aligned(1024))) char st2[kStage];
+  // K / V ring: bf16 two stages (one tile in flight; 1-2% faster than three), fp32 three
+  constexpr int NST = E::kBytes == 2 ? 2 : 3;
+  __shared__ __attribute__((aligned(1024))) char ring[NST * kStage];
   __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
 
   const int lane = lane_id();
@@ -94,8 +94,8 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
     dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
     dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
   };
-  issue(0, st0);
-  if (n_steps > 1) issue(1, st1);
+  issue(0, ring);
+  if (NST == 3 && n_steps > 1) issue(1, ring + kStage);
 
   Frag<E> qf[DS], df[DS];
 #pragma unroll
@@ -173,21 +173,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
       }
     }
   };
-  auto step = [&](auto stc, int s) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stc)::value;
-    char* cur = ST == 0 ? st0 : (ST == 1 ? st1 : st2);
-    char* nn = ST == 0 ? st2 : (ST == 1 ? st0 : st1);
-    if (s + 1 < n_steps) wait_vmcnt<kOps>();
-    else wait_vmcnt<0>();
-    barrier_keep_vm();
-    if (s + 2 < n_steps) issue(s + 2, nn);
-    compute(s, cur);
-  };
-  for (int s = 0; s < n_steps; s += 3) {
-    step(IC<0>{}, s);
-    if (s + 1 < n_steps) step(IC<1>{}, s + 1);
-    if (s + 2 < n_steps) step(IC<2>{}, s + 2);
-  }
+  ring_run<NST, kStage, kOps>(ring, n_steps, issue, compute);
 
   if (!q_ok) return;
   typename E::T* dq_row = dQ + q_off + (size_t)my_q * D;
@@ -207,13 +193,13 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
   }
 }
 
-// Key tiles: bf16 with 8 waves 64 keys (128 for D = 64: 3% faster); bf16 with 4 waves 32 keys (64
-// for D = 64), so that the three-stage ring takes at most 56 KB of LDS and two workgroups share a
-// compute unit; fp32 32 keys.
+// Key tiles: bf16 with 8 waves 64 keys (128 for D = 64: 3% faster); bf16 with 4 waves 64 keys (two
+// workgroups share a compute unit; at D = 128 4% faster than 32 keys on packed documents, at D = 64
+// 128 keys were 4-10% slower on the window workloads); fp32 32 keys.
 template <class E, int D, int NW, bool VL>
 static void launch_dq_nw(const Args& a) {
   typedef typename E::T T;
-  constexpr int KB = E::kBytes == 2 ? (NW == 4 ? (D == 64 ? 2 : 1) : (D == 64 ? 4 : 2)) : 1;
+  constexpr int KB = E::kBytes == 2 ? (NW == 4 ? 2 : (D == 64 ? 4 : 2)) : 1;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
   hipLaunchKernelGGL((dq_kernel<E, D, NW, KB, VL>), dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(NW * 64), 0,
