@@ -142,12 +142,13 @@ __global__ __launch_bounds__(kDecNW * 64) void decode_kernel(
     m = pair_max(mx) * scale_log2;  // -inf for a row that sees none of these keys
     const float neg_m = m == kNegInf ? 0.f : -m;
     Frag<E> pf[2];
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], scale_log2, neg_m));
+    add_block4(st, ps);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) pf[t] = acc_frag_sum<E>(st, t, psum);
-    l = pair_sum(psum);
+    for (int t = 0; t < 2; ++t) pf[t] = acc_frag<E>(st, t);
+    l = pair_sum(sum4(ps));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll

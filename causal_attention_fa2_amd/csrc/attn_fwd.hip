@@ -92,12 +92,18 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   const int n_steps = jt_ns + jt_hi - jt_lo + 1;
   auto tile_of = [&](int s) __attribute__((always_inline)) { return s < jt_ns ? s : jt_lo + s - jt_ns; };
 
+  const uint32_t dma_off = dma_fast_ok<E, BC, D, NW>() ? dma_lane_off<KvTile, NW>() : 0;  // whole tiles
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
     const int j0 = tile_of(s) * BC;
     if constexpr (PG) {
       const int* tab = pg.table + (size_t)b * pg.max_blocks;
       dma_tile_paged<E, BC, D, NW>(stg, K, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
       dma_tile_paged<E, BC, D, NW>(stg + KvTile::kBytes, V, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
+    } else if (dma_fast_ok<E, BC, D, NW>() && j0 + BC <= S) {
+      if constexpr (dma_fast_ok<E, BC, D, NW>()) {
+        dma_tile_fast<E, BC, D, NW>(stg, k_bg, j0, dma_off);
+        dma_tile_fast<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, dma_off);
+      }
     } else {
       dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
       dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
   wait_vmcnt<0>();  // Q fragments (and the first tiles) have landed before the loop
   float m = kNegInf;  // running max of base-2 scores
-  float l = 0.f;      // running sum of exp2(score - m)
+  float l = 0.f;      // running sum of exp2(score - m) over this lane's keys
 
   auto compute_general = [&](int j0, const char* k_lds, bool full) __attribute__((always_inline)) {
     const char* v_lds = k_lds + KvTile::kBytes;
@@ -139,24 +145,23 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     for (int db = 0; db < DB; ++db) vt[db] = TrFrag<E, KvTile>::get(v_lds, 0, 32 * db);
     __builtin_amdgcn_sched_barrier(0);
 
-    // Row max of the raw scores (scale > 0 commutes with max); masked keys become -inf.
-    float mx = kNegInf;
-    if (full) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-    } else {
+    // Row max of the raw scores (scale > 0 commutes with max); masked keys become -inf, in place
+    // (the unmasked scores keep their registers, so the two paths need no copies to merge).
+    if (!full) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + 32 * kb + acc_row(r);
-          if (!visible(my_p, j, S, causal, window, sink) || (VL && j < ds_lane)) st[kb][r] = kNegInf;
-          mx = fmaxf(mx, st[kb][r]);
+          mask_neg_inf(st[kb], r, visible(my_p, j, S, causal, window, sink) && !(VL && j < ds_lane));
         }
       }
     }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
     mx = pair_max(mx) * scale_log2;
     // Rescale a row only when its max grew by more than 2^8 (exponents stay <= 8, so P <= 256
     // and every sum stays far from overflow; O / l does not depend on the reference value). The
@@ -172,18 +177,19 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     m = grow ? mx : m;
     const float neg_m = m == kNegInf ? 0.f : -m;  // row with nothing visible yet: all P are 0
 
-    // P^T = exp2(S^T * scale*log2e - m) as element-type fragments; the row sum uses the same
-    // rounded values that enter O^T, so the normaliser matches the numerator.
+    // P^T = exp2(S^T * scale*log2e - m) as element-type fragments; the row sum adds the fp32
+    // values (add_block4 order) before they are rounded for the product.
     Frag<E> pf[KB][2];
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kb][r] = __builtin_amdgcn_exp2f(fmaf(st[kb][r], scale_log2, neg_m));
+      add_block4(st[kb], ps);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) pf[kb][t] = acc_frag_sum<E>(st[kb], t, psum);
+      for (int t = 0; t < 2; ++t) pf[kb][t] = acc_frag<E>(st[kb], t);
     }
-    l += pair_sum(psum);
+    l += sum4(ps);  // this lane's keys; the partner lane's half of the row is added at the end
 
     // O^T += V^T P^T, contraction over the tile's keys in the accumulator's row order; the next
     // 16 keys' V^T fragments are requested under the current products.
@@ -217,6 +223,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
 
   ring_run<NST, kStage, kOps>(ring, n_steps, issue, compute);
 
+  l = pair_sum(l);
   if (!q_ok) return;
   const float inv_l = 1.f / l;
   typename E::T* o_row = O + ((size_t)(b * Hq + h) * Sq + my_q) * D;

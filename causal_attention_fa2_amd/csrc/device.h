@@ -100,37 +100,24 @@ template <> __device__ __forceinline__ Frag<F32> acc_frag<F32>(const f32x16_t& a
   return f;
 }
 
-// Accumulator registers 8t..8t+7 as an element-type fragment, adding the 8 rounded values to
-// `sum`. For bf16 the sum is four v_dot2c_f32_bf16 against (1, 1) on the packed words. The words
-// are kept as separate scalars before they form the vector: feeding elements extracted from the
-// assembled u32x4 to the dot2 builtin was miscompiled (the same word read four times).
-__device__ __forceinline__ Frag<BF16> acc_frag_sum(const f32x16_t& a, int t, float& sum) {
-  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
-  const uint32_t w0 = pack_bf16x2(a[8 * t + 0], a[8 * t + 1]);
-  const uint32_t w1 = pack_bf16x2(a[8 * t + 2], a[8 * t + 3]);
-  const uint32_t w2 = pack_bf16x2(a[8 * t + 4], a[8 * t + 5]);
-  const uint32_t w3 = pack_bf16x2(a[8 * t + 6], a[8 * t + 7]);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(ones, __builtin_bit_cast(bf16x2_t, w0), sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(ones, __builtin_bit_cast(bf16x2_t, w1), sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(ones, __builtin_bit_cast(bf16x2_t, w2), sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(ones, __builtin_bit_cast(bf16x2_t, w3), sum, false);
-  Frag<BF16> f;
-  f.v = u32x4_t{w0, w1, w2, w3};
-  return f;
-}
-__device__ __forceinline__ Frag<F32> acc_frag_sum(const f32x16_t& a, int t, float& sum, F32*) {
-  Frag<F32> f;
+// Adds the 16 exponentials of one 32-key block (one accumulator) into four running partial sums in
+// register order: sum[r % 4] += p[r]. Summing the fp32 values before they are rounded for the P V
+// product keeps the row sum on plain VALU adds (v_dot2c_f32_bf16 on the packed words runs about
+// 2.5x slower while another wave of the SIMD issues matrix products). Every forward and decode
+// kernel sums in this order, so rows computed by different kernels agree bit for bit.
+__device__ __forceinline__ void add_block4(const f32x16_t& p, float (&sum)[4]) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f.lo[e] = a[8 * t + e];
-    f.hi[e] = a[8 * t + 4 + e];
-    sum += f.lo[e] + f.hi[e];
-  }
-  return f;
+  for (int r = 0; r < 16; ++r) sum[r & 3] += p[r];
 }
-template <class E> __device__ __forceinline__ Frag<E> acc_frag_sum(const f32x16_t& a, int t, float& sum) {
-  if constexpr (E::kBytes == 2) return acc_frag_sum(a, t, sum);
-  else return acc_frag_sum(a, t, sum, (F32*)nullptr);
+__device__ __forceinline__ float sum4(const float (&sum)[4]) { return (sum[0] + sum[1]) + (sum[2] + sum[3]); }
+
+// v[r] = keep ? v[r] : -inf, written back into the element's own register (no copy of the
+// surviving values).
+__device__ __forceinline__ void mask_neg_inf(f32x16_t& v, int r, bool keep) {
+  const float ninf = kNegInf;
+  float x = v[r];
+  asm("v_cndmask_b32 %0, %1, %0, %2" : "+v"(x) : "v"(ninf), "s"(__builtin_amdgcn_ballot_w64(keep)));
+  v[r] = x;
 }
 
 // ---------------------------------------------------------------- global fragments
@@ -242,6 +229,47 @@ template <class Tile> struct TrFrag<F32, Tile> {
     return f;
   }
 };
+
+// Lane offsets for fragment reads from precomputed addresses (bf16 tiles). The swizzle depends
+// only on row % 16, so moving by whole 16-row groups adds a constant: the row fragment of row
+// (lane % 32) + 32 kb, step s, sits at row_frag_off(s) + 32 kb * kRowBytes, and the two halves of
+// the transposed fragment for rows 16 k2 .. and column block n0 at tr_frag_off(n0, x) +
+// 16 k2 * kRowBytes (x = 0: rows +0..7, x = 1: rows +8..15). Kernels keep these few offsets in
+// registers and put the block and ring-stage parts into the instructions' immediate offsets.
+template <class Tile>
+__device__ __forceinline__ int row_frag_off(int s) {
+  return Tile::chunk_off(lane_id() & 31, 2 * s + (lane_id() >> 5));
+}
+template <class Tile>
+__device__ __forceinline__ int tr_frag_off(int n0, int x) {
+  const int l = lane_id();
+  const int s = l & 15;
+  const int col = n0 + 16 * ((l >> 4) & 1) + 4 * (s & 3);
+  const int row = 4 * (l >> 5) + (s >> 2) + 8 * x;
+  return Tile::chunk_off(row, col >> 3) + (s & 1) * 8;
+}
+// Fragment reads at LDS byte address `a` (a wave's per-lane base, see above) plus a constant.
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+__device__ __forceinline__ Frag<BF16> lds_row_frag(uint32_t a) {
+  Frag<BF16> f;
+  f.v = *(const lds_u32x4_t*)(uintptr_t)a;
+  return f;
+}
+__device__ __forceinline__ Frag<BF16> lds_tr_frag(uint32_t pa, uint32_t pb) {
+  s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)pa);
+  s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)pb);
+  Frag<BF16> f;
+  u32x2_t ua = __builtin_bit_cast(u32x2_t, a);
+  u32x2_t ub = __builtin_bit_cast(u32x2_t, b);
+  f.v = u32x4_t{ua[0], ua[1], ub[0], ub[1]};
+  return f;
+}
+// x, as a value the compiler cannot take apart: an address formed from it plus a constant keeps
+// the constant in the instruction's offset field instead of one register per constant.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
+}
 
 // Cooperative copy of rows [row0, row0 + ROWS) of a [S, D] matrix into an LDS tile; rows at or
 // beyond S are written as zeros (so masked keys contribute exact zeros, never NaN).
@@ -359,6 +387,39 @@ __device__ __forceinline__ void dma_tile(char* lds, const typename E::T* __restr
 }
 template <class E, int ROWS, int D, int NW>
 constexpr int dma_tile_ops() { return LdsTile<E, ROWS, D>::kBytes / 1024 / NW; }
+
+// The same copy for whole tiles with the global address split into a wave-uniform base (SGPRs)
+// and a per-lane 32-bit offset that depends only on the lane and the 1 KB block: a tile row
+// group of 64 * 16 / kRowBytes rows per block, and block n * NW + w of this wave lies
+// n * NW * 1024 bytes further on in both the tile and LDS (the swizzle repeats every 16 rows).
+// `lane_off` = dma_lane_off<Tile, NW>() computed once; no per-copy vector arithmetic. Rows at or
+// past S need the clamped copy (dma_tile).
+template <class Tile, int NW>
+__device__ __forceinline__ uint32_t dma_lane_off() {
+  const int c = wave_id() * 64 + lane_id();
+  const int r = c / Tile::kChunks;
+  const int pos = c % Tile::kChunks;
+  return (uint32_t)(r * Tile::kRowBytes + ((pos ^ Tile::swz(r)) << 4));
+}
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+}
+template <class E, int ROWS, int D, int NW>
+constexpr bool dma_fast_ok() {
+  return (LdsTile<E, ROWS, D>::kBytes / 1024) % NW == 0 && (NW * 1024) % (16 * LdsTile<E, ROWS, D>::kRowBytes) == 0;
+}
+template <class E, int ROWS, int D, int NW>
+__device__ __forceinline__ void dma_tile_fast(char* lds, const typename E::T* __restrict__ src, int row0,
+                                              uint32_t lane_off) {
+  typedef LdsTile<E, ROWS, D> Tile;
+  constexpr int kBlocks = Tile::kBytes / 1024;
+  static_assert(kBlocks % NW == 0 && (NW * 1024) % (16 * Tile::kRowBytes) == 0, "blocks repeat the swizzle");
+  const char* tile = reinterpret_cast<const char*>(src + (size_t)row0 * D);
+  const uint32_t base = lds_addr(lds) + wave_id() * 1024;
+#pragma unroll
+  for (int n = 0; n < kBlocks / NW; ++n) dma16_s(lane_off, tile + n * NW * 1024, base + n * NW * 1024);
+}
 
 // The same copy from a paged cache: row t of the sequence lives in physical block tab[t >> shift]
 // of a [nblocks, Hkv, 2^shift, D] pool, head g, slot t & (2^shift - 1). Block sizes are powers of
