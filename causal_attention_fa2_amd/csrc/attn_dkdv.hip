@@ -75,11 +75,20 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   // Query tiles are visited from the last one down, so the workgroups of one KV head (which all
   // end at the last query tile) sweep the same Q / dO tiles at about the same time. Steps run
   // head by head; (hh, it) is a step's head offset and query-tile counter.
+  constexpr bool kFast = dma_fast_ok<E, BR, D, NW>();
+  const uint32_t dma_off = kFast ? dma_lane_off<QTile, NW>() : 0;  // whole tiles: scalar base + offset
   auto issue = [&](int hh, int it, char* stg) __attribute__((always_inline)) {
     const int i0 = (lo + nq - 1 - it) * BR;
     const size_t bh = (size_t)b * Hq + h0 + hh;
-    dma_tile<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, Sq);
-    dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, Sq);
+    if (kFast && i0 + BR <= Sq) {
+      if constexpr (kFast) {
+        dma_tile_fast<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, dma_off);
+        dma_tile_fast<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, dma_off);
+      }
+    } else {
+      dma_tile<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, Sq);
+      dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, Sq);
+    }
     if (w == 0) dma_row_floats(stg + kRowOff, LSE2 + bh * Sq, i0, Sq);
     if (w == 1) dma_row_floats(stg + kRowOff + 256, delta + bh * Sq, i0, Sq);
   };
@@ -394,11 +403,20 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     n_steps = hpg * nq;
   };
   // Query tiles run from the last one down, head by head; (hh, it) = head offset, tile counter.
+  constexpr bool kFast = dma_fast_ok<E, BR, D, NW>();
+  const uint32_t dma_off = kFast ? dma_lane_off<QTile, NW>() : 0;  // whole tiles: scalar base + offset
   auto issue = [&](int hh, int it, char* stg) __attribute__((always_inline)) {
     const int i0 = (lo + nq - 1 - it) * BR;
     const size_t bh = (size_t)b * Hq + h0 + hh;
-    dma_tile<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, Sq);
-    dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, Sq);
+    if (kFast && i0 + BR <= Sq) {
+      if constexpr (kFast) {
+        dma_tile_fast<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, dma_off);
+        dma_tile_fast<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, dma_off);
+      }
+    } else {
+      dma_tile<E, BR, D, NW>(stg, Q + bh * Sq * D, i0, Sq);
+      dma_tile<E, BR, D, NW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, Sq);
+    }
     if (w < kRowWaves) {  // wave 2c copies lse rows 64c.., wave 2c+1 the delta rows 64c..
       const int c = w >> 1;
       dma_row_floats(stg + kRowOff + (w & 1) * 4 * BR + 256 * c, ((w & 1) ? delta : LSE2) + bh * Sq, i0 + 64 * c, Sq);
@@ -411,163 +429,162 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     }
   };
 
-  Frag<E> kvf[DS];   // K (S role) or V (dP role) rows of this pair's keys: the B operand
-  f32x16_t acc[DB];  // dV (S role) or dK (dP role); register r holds key kw + acc_row(r)
-  auto load_kv = [&]() __attribute__((always_inline)) {
-    const int my_k = kt * BC + 32 * pw + l32;
-    const bool ok = my_k < S;
-    if constexpr (VL) de_lane = doc_end(cu_s, docs.n, imin_(my_k, S - 1));
-    const uint16_t* src = (srole ? K : V) + kv_off + (size_t)my_k * D + 8 * half;
+  // Everything below is specialised on the wave's role (fixed for the whole kernel), so the two
+  // roles' values never meet in one register allocation: no copies where the paths rejoin.
+  auto run = [&](auto role_c) __attribute__((always_inline)) {
+    constexpr bool SR = decltype(role_c)::value != 0;
+    Frag<E> kvf[DS];   // K (S role) or V (dP role) rows of this pair's keys: the B operand
+    f32x16_t acc[DB];  // dV (S role) or dK (dP role); register r holds key kw + acc_row(r)
+    auto load_kv = [&]() __attribute__((always_inline)) {
+      const int my_k = kt * BC + 32 * pw + l32;
+      const bool ok = my_k < S;
+      if constexpr (VL) de_lane = doc_end(cu_s, docs.n, imin_(my_k, S - 1));
+      const uint16_t* src = (SR ? K : V) + kv_off + (size_t)my_k * D + 8 * half;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) kvf[s] = load_frag_global(src + 16 * s, ok);
+      for (int s2 = 0; s2 < DS; ++s2) kvf[s2] = load_frag_global(src + 16 * s2, ok);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
-  };
-  auto flush = [&]() __attribute__((always_inline)) {
-    const int kw = kt * BC + 32 * pw;
-    const size_t nkv = (size_t)B * Hkv * S * D;
-    const float mul = srole ? 1.f : scale;
-    // sink split: key tile 0 goes to this chunk's slot [chunk][hp][bg][dK, dV][BC][D]
-    const bool to_x = nc > 1 && kt == 0;
-    float* xs_slot = to_x ? xpart + ((((size_t)chunk * hs + hp) * BG + bg) * 2 + (srole ? 1 : 0)) * BC * D : nullptr;
+      for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+    };
+    auto flush = [&]() __attribute__((always_inline)) {
+      const int kw = kt * BC + 32 * pw;
+      const size_t nkv = (size_t)B * Hkv * S * D;
+      const float mul = SR ? 1.f : scale;
+      // sink split: key tile 0 goes to this chunk's slot [chunk][hp][bg][dK, dV][BC][D]
+      const bool to_x = nc > 1 && kt == 0;
+      float* xs_slot = to_x ? xpart + ((((size_t)chunk * hs + hp) * BG + bg) * 2 + (SR ? 1 : 0)) * BC * D : nullptr;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kw + acc_row(r);
-        if (key >= S) continue;
-        const size_t o = kv_off + (size_t)key * D + 32 * db + l32;
-        if (to_x) {
-          xs_slot[(size_t)key * D + 32 * db + l32] = acc[db][r];
-        } else if (hs > 1) {
-          part[(size_t)(2 * hp + (srole ? 1 : 0)) * nkv + o] = acc[db][r];
-        } else {
-          (srole ? dV : dK)[o] = (uint16_t)bf16_bits(acc[db][r] * mul);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kw + acc_row(r);
+          if (key >= S) continue;
+          const size_t o = kv_off + (size_t)key * D + 32 * db + l32;
+          if (to_x) {
+            xs_slot[(size_t)key * D + 32 * db + l32] = acc[db][r];
+          } else if (hs > 1) {
+            part[(size_t)(2 * hp + (SR ? 1 : 0)) * nkv + o] = acc[db][r];
+          } else {
+            (SR ? dV : dK)[o] = (uint16_t)bf16_bits(acc[db][r] * mul);
+          }
         }
       }
-    }
-  };
+    };
 
-  auto compute = [&](int it, const char* q_lds) __attribute__((always_inline)) {
-    const char* do_lds = q_lds + QTile::kBytes;
-    const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
-    const float* dl_lds = lse_lds + BR;
-    const int i0 = (lo + nq - 1 - it) * BR;
-    const int p0 = i0 + qoff;  // position of the tile's first row
-    const int kw = kt * BC + 32 * pw;
-    const int my_k = kw + l32;
-    f32x16_t xs[QB];  // S -> P (S role) or dP -> dS (dP role)
-    bool act[QB];
-    // Phase 1: S = Q K^T and P (S role), dP = dO V^T (dP role).
+    // One 64-row (128 for D = 64) query tile. Blocks of 32 rows that see none of this pair's keys
+    // (the causal diagonal, window edges) are computed like partial ones: every P is 0, so they
+    // add exact zeros to dV and dK.
+    auto compute = [&](int it, const char* q_lds) __attribute__((always_inline)) {
+      const char* do_lds = q_lds + QTile::kBytes;
+      const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
+      const float* dl_lds = lse_lds + BR;
+      const int i0 = (lo + nq - 1 - it) * BR;
+      const int p0 = i0 + qoff;  // position of the tile's first row
+      const int kw = kt * BC + 32 * pw;
+      const int my_k = kw + l32;
+      f32x16_t xs[QB];  // S -> P (S role) or dP -> dS (dP role)
+      // Phase 1: S = Q K^T and P (S role), dP = dO V^T (dP role).
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int r0 = p0 + 32 * qb;
-      act[qb] = !block_empty(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
-      if constexpr (VL) act[qb] = act[qb] && r0 < __builtin_amdgcn_readlane(de_lane, 31);
-      if (!act[qb]) continue;
-      const char* src = srole ? q_lds : do_lds;
-      Frag<E> fr[DS];
+      for (int qb = 0; qb < QB; ++qb) {
+        const int r0 = p0 + 32 * qb;
+        Frag<E> fr[DS];
 #pragma unroll
-      for (int s2 = 0; s2 < DS; ++s2) fr[s2] = RowFrag<E, QTile>::get(src, 32 * qb + l32, s2);
-      __builtin_amdgcn_sched_barrier(0);
-      xs[qb] = f32x16_t{};
+        for (int s2 = 0; s2 < DS; ++s2) fr[s2] = RowFrag<E, QTile>::get(SR ? q_lds : do_lds, 32 * qb + l32, s2);
+        __builtin_amdgcn_sched_barrier(0);
+        xs[qb] = f32x16_t{};
 #pragma unroll
-      for (int s2 = 0; s2 < DS; ++s2) mma(xs[qb], fr[s2], kvf[s2]);
-      if (srole) {
-        bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
-        if constexpr (VL) full = full && r0 + 31 < __builtin_amdgcn_readlane(de_lane, 0);
-        auto softmax = [&](auto maskc) __attribute__((always_inline)) {
+        for (int s2 = 0; s2 < DS; ++s2) mma(xs[qb], fr[s2], kvf[s2]);
+        if constexpr (SR) {
+          bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
+          if constexpr (VL) full = full && r0 + 31 < __builtin_amdgcn_readlane(de_lane, 0);
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int rb = 32 * qb + 8 * r4 + 4 * half;  // registers 4*r4 .. 4*r4+3: rows rb .. rb+3
             const f32x4_t lse4 = *reinterpret_cast<const f32x4_t*>(lse_lds + rb);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int r = 4 * r4 + c;
-              float p = __builtin_amdgcn_exp2f(fmaf(xs[qb][r], scale_log2, -lse4[c]));
-              if constexpr (decltype(maskc)::value) {
-                const int i = p0 + rb + c;
-                if (!visible(i, my_k, S, causal, window, sink) || (VL && i >= de_lane)) p = 0.f;
-              }
-              xs[qb][r] = p;
+            for (int c = 0; c < 4; ++c)
+              xs[qb][4 * r4 + c] = __builtin_amdgcn_exp2f(fmaf(xs[qb][4 * r4 + c], scale_log2, -lse4[c]));
+          }
+          if (!full) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int i = p0 + 32 * qb + acc_row(r);
+              mask_zero(xs[qb], r, visible(i, my_k, S, causal, window, sink) && !(VL && i >= de_lane));
             }
           }
-        };
-        if (full) softmax(IC<0>{});
-        else softmax(IC<1>{});
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          *reinterpret_cast<u32x4_t*>(pslot + qb * kPBlock + t * 1024) = acc_frag<E>(xs[qb], t).v;
-      }
-    }
-    barrier_keep_vm();  // the P blocks are in LDS
-    // Phase 2: dV += P^T dO (S role); dS = P o (dP - delta), dK += dS^T Q (dP role).
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (!act[qb]) continue;
-      const char* tsrc = srole ? do_lds : q_lds;
-      if (!srole) {
-        const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pslot + qb * kPBlock);
-        const u32x4_t pb = *reinterpret_cast<const u32x4_t*>(pslot + qb * kPBlock + 1024);
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int rb = 32 * qb + 8 * r4 + 4 * half;
-          const f32x4_t dl4 = *reinterpret_cast<const f32x4_t*>(dl_lds + rb);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = 4 * r4 + c;
-            const uint32_t word = (r < 8 ? pa : pb)[(r & 7) >> 1];
-            const float p = __uint_as_float((r & 1) ? (word & 0xFFFF0000u) : (word << 16));
-            xs[qb][r] = p * (xs[qb][r] - dl4[c]);
-          }
+          for (int t = 0; t < 2; ++t)
+            *reinterpret_cast<u32x4_t*>(pslot + qb * kPBlock + t * 1024) = acc_frag<E>(xs[qb], t).v;
         }
       }
+      barrier_keep_vm();  // the P blocks are in LDS
+      // Phase 2: dV += P^T dO (S role); dS = P o (dP - delta), dK += dS^T Q (dP role).
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        Frag<E> tr[DB];  // dO^T (S role) or Q^T (dP role), rows 32*qb + 16t ..
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (!SR) {
+          const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pslot + qb * kPBlock);
+          const u32x4_t pb = *reinterpret_cast<const u32x4_t*>(pslot + qb * kPBlock + 1024);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) tr[db] = TrFrag<E, QTile>::get(tsrc, 32 * qb + 16 * t, 32 * db);
-        const Frag<E> af = acc_frag<E>(xs[qb], t);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int rb = 32 * qb + 8 * r4 + 4 * half;
+            const f32x4_t dl4 = *reinterpret_cast<const f32x4_t*>(dl_lds + rb);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) mma(acc[db], af, tr[db]);
+            for (int c = 0; c < 4; ++c) {
+              const int r = 4 * r4 + c;
+              const uint32_t word = (r < 8 ? pa : pb)[(r & 7) >> 1];
+              const float p = __uint_as_float((r & 1) ? (word & 0xFFFF0000u) : (word << 16));
+              xs[qb][r] = p * (xs[qb][r] - dl4[c]);
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          Frag<E> tr[DB];  // dO^T (S role) or Q^T (dP role), rows 32*qb + 16t ..
+#pragma unroll
+          for (int db = 0; db < DB; ++db) tr[db] = TrFrag<E, QTile>::get(SR ? do_lds : q_lds, 32 * qb + 16 * t, 32 * db);
+          const Frag<E> af = acc_frag<E>(xs[qb], t);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) mma(acc[db], af, tr[db]);
+        }
       }
-    }
-  };
+    };
 
-  int ch, ct, ih, iq;
-  // Two-stage ring (one tile in flight): step s waits for its own tile, then, once every wave is
-  // past step s - 1, copies tile s + 1 into the stage step s - 1 used. 2-4% faster than three
-  // stages with two tiles in flight, on every workload measured.
-  auto step = [&](auto stc, int s) __attribute__((always_inline)) {
-    constexpr int ST = decltype(stc)::value;
-    char* cur = ST == 0 ? st0 : st1;
-    char* nn = ST == 0 ? st1 : st0;
-    wait_vmcnt<0>();
-    barrier_keep_vm();
-    if (s + 1 < n_steps) {
-      issue(ih, iq, nn);
-      advance(ih, iq);
+    int ch, ct, ih, iq;
+    // Two-stage ring (one tile in flight): step s waits for its own tile, then, once every wave is
+    // past step s - 1, copies tile s + 1 into the stage step s - 1 used. 2-4% faster than three
+    // stages with two tiles in flight, on every workload measured.
+    auto step = [&](auto stc, int s) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stc)::value;
+      char* cur = ST == 0 ? st0 : st1;
+      char* nn = ST == 0 ? st1 : st0;
+      wait_vmcnt<0>();
+      barrier_keep_vm();
+      if (s + 1 < n_steps) {
+        issue(ih, iq, nn);
+        advance(ih, iq);
+      }
+      compute(ct, cur);
+      advance(ch, ct);
+    };
+    const int n_seg = two ? 2 : 1;
+    for (int seg = 0; seg < n_seg; ++seg) {
+      if (seg) barrier_keep_vm();  // every wave is done with the previous segment's stages
+      set_segment(seg ? tb : ta);
+      load_kv();
+      ch = 0, ct = 0, ih = 0, iq = 0;
+      if (n_steps > 0) {
+        issue(ih, iq, st0);
+        advance(ih, iq);
+      }
+      wait_vmcnt<0>();
+      for (int s = 0; s < n_steps; s += 2) {
+        step(IC<0>{}, s);
+        if (s + 1 < n_steps) step(IC<1>{}, s + 1);
+      }
+      flush();
     }
-    compute(ct, cur);
-    advance(ch, ct);
   };
-  const int n_seg = two ? 2 : 1;
-  for (int seg = 0; seg < n_seg; ++seg) {
-    if (seg) barrier_keep_vm();  // every wave is done with the previous segment's stages
-    set_segment(seg ? tb : ta);
-    load_kv();
-    ch = 0, ct = 0, ih = 0, iq = 0;
-    if (n_steps > 0) {
-      issue(ih, iq, st0);
-      advance(ih, iq);
-    }
-    wait_vmcnt<0>();
-    for (int s = 0; s < n_steps; s += 2) {
-      step(IC<0>{}, s);
-      if (s + 1 < n_steps) step(IC<1>{}, s + 1);
-    }
-    flush();
-  }
+  if (srole) run(IC<1>{});
+  else run(IC<0>{});
 }
 
 // Adds the hs head-part partials. Rows below skip_rows of every (batch, KV head) are left to

@@ -120,6 +120,13 @@ __device__ __forceinline__ void mask_neg_inf(f32x16_t& v, int r, bool keep) {
   v[r] = x;
 }
 
+// v[r] = keep ? v[r] : 0, in place.
+__device__ __forceinline__ void mask_zero(f32x16_t& v, int r, bool keep) {
+  float x = v[r];
+  asm("v_cndmask_b32 %0, 0, %0, %1" : "+v"(x) : "s"(__builtin_amdgcn_ballot_w64(keep)));
+  v[r] = x;
+}
+
 // ---------------------------------------------------------------- global fragments
 // 8 consecutive elements from global memory (16 B for bf16, 32 B for f32), or zeros.
 __device__ __forceinline__ Frag<BF16> load_frag_global(const uint16_t* p, bool ok) {
@@ -401,9 +408,16 @@ __device__ __forceinline__ uint32_t dma_lane_off() {
   const int pos = c % Tile::kChunks;
   return (uint32_t)(r * Tile::kRowBytes + ((pos ^ Tile::swz(r)) << 4));
 }
+// `sbase` must be the same for every lane of the wave; it is moved to scalar registers here.
 __device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  // (readfirstlane returns int: both halves are taken back to uint32_t before widening, so the
+  // low half is zero-extended, not sign-extended)
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory", "m0");
+               :: "v"(voff), "s"(sa), "s"(lds_base) : "memory", "m0");
 }
 template <class E, int ROWS, int D, int NW>
 constexpr bool dma_fast_ok() {
