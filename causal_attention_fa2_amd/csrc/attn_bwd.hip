@@ -89,10 +89,19 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
   if constexpr (VL) jt_lo = imax_(jt_lo, doc_start(cu_s, docs.n, q0 + off) / BC);  // no sinks here
   const int n_steps = jt_ns + jt_hi - jt_lo + 1;
   auto tile_of = [&](int s) __attribute__((always_inline)) { return s < jt_ns ? s : jt_lo + s - jt_ns; };
+  constexpr bool kFast = dma_fast_ok<E, BC, D, NW>();
+  const uint32_t dma_off = kFast ? dma_lane_off<KvTile, NW>() : 0;  // whole tiles: scalar base + offset
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
     const int j0 = tile_of(s) * BC;
-    dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
-    dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
+    if (kFast && j0 + BC <= S) {
+      if constexpr (kFast) {
+        dma_tile_fast<E, BC, D, NW>(stg, k_bg, j0, dma_off);
+        dma_tile_fast<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, dma_off);
+      }
+    } else {
+      dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
+      dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
+    }
   };
   issue(0, ring);
   if (NST == 3 && n_steps > 1) issue(1, ring + kStage);
@@ -149,21 +158,21 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
         mma(st, RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s2), qf[s2]);
         mma(dpt, RowFrag<E, KvTile>::get(v_lds, 32 * kb + l32, s2), df[s2]);
       }
-      auto grad = [&](auto maskc) __attribute__((always_inline)) {
-        int mp = 0;  // this lane's position, re-derived inside the masked path only
-        if constexpr (decltype(maskc)::value) mp = opaque(my_p);
+      // P = exp2(S * scale * log2 e - lse * log2 e), masked to 0 in place on partial tiles (one
+      // code path, so no register copies where masked and unmasked tiles rejoin), then
+      // dS = P o (dP - delta).
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = __builtin_amdgcn_exp2f(fmaf(st[r], scale_log2, nlse2));
+      if (!full) {
+        const int mp = opaque(my_p);  // this lane's position, re-derived inside the masked path only
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(fmaf(st[r], scale_log2, nlse2));
-          if constexpr (decltype(maskc)::value) {
-            const int j = j0 + 32 * kb + acc_row(r);
-            if (!visible(mp, j, S, causal, window, sink) || (VL && j < ds_lane)) p = 0.f;
-          }
-          st[r] = p * (dpt[r] - dl);
+          const int j = j0 + 32 * kb + acc_row(r);
+          mask_zero(st, r, visible(mp, j, S, causal, window, sink) && !(VL && j < ds_lane));
         }
-      };
-      if (full) grad(IC<0>{});
-      else grad(IC<1>{});
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[r] = st[r] * (dpt[r] - dl);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const Frag<E> sf = acc_frag<E>(st, t);

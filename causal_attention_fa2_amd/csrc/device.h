@@ -237,47 +237,6 @@ template <class Tile> struct TrFrag<F32, Tile> {
   }
 };
 
-// Lane offsets for fragment reads from precomputed addresses (bf16 tiles). The swizzle depends
-// only on row % 16, so moving by whole 16-row groups adds a constant: the row fragment of row
-// (lane % 32) + 32 kb, step s, sits at row_frag_off(s) + 32 kb * kRowBytes, and the two halves of
-// the transposed fragment for rows 16 k2 .. and column block n0 at tr_frag_off(n0, x) +
-// 16 k2 * kRowBytes (x = 0: rows +0..7, x = 1: rows +8..15). Kernels keep these few offsets in
-// registers and put the block and ring-stage parts into the instructions' immediate offsets.
-template <class Tile>
-__device__ __forceinline__ int row_frag_off(int s) {
-  return Tile::chunk_off(lane_id() & 31, 2 * s + (lane_id() >> 5));
-}
-template <class Tile>
-__device__ __forceinline__ int tr_frag_off(int n0, int x) {
-  const int l = lane_id();
-  const int s = l & 15;
-  const int col = n0 + 16 * ((l >> 4) & 1) + 4 * (s & 3);
-  const int row = 4 * (l >> 5) + (s >> 2) + 8 * x;
-  return Tile::chunk_off(row, col >> 3) + (s & 1) * 8;
-}
-// Fragment reads at LDS byte address `a` (a wave's per-lane base, see above) plus a constant.
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-__device__ __forceinline__ Frag<BF16> lds_row_frag(uint32_t a) {
-  Frag<BF16> f;
-  f.v = *(const lds_u32x4_t*)(uintptr_t)a;
-  return f;
-}
-__device__ __forceinline__ Frag<BF16> lds_tr_frag(uint32_t pa, uint32_t pb) {
-  s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)pa);
-  s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)pb);
-  Frag<BF16> f;
-  u32x2_t ua = __builtin_bit_cast(u32x2_t, a);
-  u32x2_t ub = __builtin_bit_cast(u32x2_t, b);
-  f.v = u32x4_t{ua[0], ua[1], ub[0], ub[1]};
-  return f;
-}
-// x, as a value the compiler cannot take apart: an address formed from it plus a constant keeps
-// the constant in the instruction's offset field instead of one register per constant.
-__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
-  asm("" : "+v"(x));
-  return x;
-}
-
 // Cooperative copy of rows [row0, row0 + ROWS) of a [S, D] matrix into an LDS tile; rows at or
 // beyond S are written as zeros (so masked keys contribute exact zeros, never NaN).
 template <class E, class Tile, int ROWS, int D, int NTHREADS>
