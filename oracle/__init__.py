@@ -5,7 +5,7 @@ import it. It shares no code with the HIP path and imports nothing from the prod
 """
 from .attention import (  # noqa: F401
     cols_dkdv, backward, document_of, forward, forward_backward, head_rows, kv_head, probabilities,
-    rows_dq, rows_forward, visible_count, visible_mask,
+    rows_dq, rows_forward, visible_mask,
 )
 from .compare import rel_l2  # noqa: F401
 from .paged import gather_sequence, paged_forward  # noqa: F401

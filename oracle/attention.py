@@ -59,7 +59,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "kv_head", "document_of", "visible_mask", "visible_count", "head_rows", "forward", "backward",
+    "kv_head", "document_of", "visible_mask", "head_rows", "forward", "backward",
     "forward_backward", "probabilities", "rows_forward", "rows_dq", "cols_dkdv",
 ]
 
@@ -113,11 +113,6 @@ def visible_mask(rows, cols, causal: bool, window: int, offset: int = 0, sink: i
     if docs is not None:
         m &= document_of(i, docs) == document_of(j, docs)
     return m
-
-
-def visible_count(i: int, S: int, causal: bool, window: int, offset: int = 0, sink: int = 0) -> int:
-    """Number of the S keys visible to query i (counted from the mask definition)."""
-    return int(visible_mask([i], np.arange(S), causal, window, offset, sink).sum())
 
 
 def head_rows(qh, kh, vh, rows, causal, window, scale, doh=None, offset=0, sink=0, docs=None):
@@ -230,24 +225,49 @@ def rows_dq(q, k, v, do, b, h, rows, causal=True, window=0, scale=None, sink=0, 
 
 
 def cols_dkdv(q, k, v, do, b, g, cols, causal=True, window=0, scale=None, row_block=256, sink=0,
-              cu_seqlens=None):
+              cu_seqlens=None, progress=None):
     """dK[b, g, cols] and dV[b, g, cols]: sums over every query head of group g and every
-    query row that can see at least one of `cols`."""
+    query row that can see at least one of `cols`.
+
+    Per block of query rows only the span of keys that some row of the block can see is
+    materialised (masked entries are exact zeros, so leaving them out changes no sum), and
+    delta_i is taken from its definition <dO_i, O_i>, so the dP / dS entries are formed only in
+    the requested columns. Each row's softmax still runs over all of its visible keys.
+    progress(done, total), if given, is called after each block of rows."""
     B, Hq, Hkv, S, Sk, D = _check(q, k, v, causal, window, sink)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     cols = np.asarray(cols, dtype=np.int64)
     G = Hq // Hkv
     kh, vh = _f64(k[b, g], v[b, g])
     docs = None if cu_seqlens is None else cu_seqlens[b]
-    need = visible_mask(np.arange(S), cols, causal, window, Sk - S, sink, docs).any(axis=1)
+    off = Sk - S
+    need = visible_mask(np.arange(S), cols, causal, window, off, sink, docs).any(axis=1)
     rows_all = np.nonzero(need)[0]
     dK = np.zeros((cols.size, D))
     dV = np.zeros((cols.size, D))
-    for h in range(g * G, (g + 1) * G):
-        qh, doh = _f64(q[b, h], do[b, h])
-        for r0 in range(0, rows_all.size, row_block):
-            rows = rows_all[r0:r0 + row_block]
-            t = head_rows(qh, kh, vh, rows, causal, window, scale, doh, Sk - S, sink, docs)
-            dK += scale * (t["dS"][:, cols].T @ qh[rows])
-            dV += t["P"][:, cols].T @ doh[rows]
+    heads = [_f64(q[b, h], do[b, h]) for h in range(g * G, (g + 1) * G)]
+    n_blocks = (rows_all.size + row_block - 1) // row_block
+    for n, r0 in enumerate(range(0, rows_all.size, row_block)):
+        rows = rows_all[r0:r0 + row_block]
+        mask = visible_mask(rows, np.arange(Sk), causal, window, off, sink, docs)
+        seen = np.nonzero(mask.any(axis=0))[0]
+        c_lo, c_hi = int(seen[0]), int(seen[-1]) + 1            # every visible key lies in [c_lo, c_hi)
+        mask = mask[:, c_lo:c_hi]
+        inside = (cols >= c_lo) & (cols < c_hi)
+        for qh, doh in heads:
+            x = scale * (qh[rows] @ kh[c_lo:c_hi].T)            # scaled scores of the span
+            x = np.where(mask, x, -np.inf)
+            m = x.max(axis=1, keepdims=True)
+            e = np.exp(x - m)
+            p = e / e.sum(axis=1, keepdims=True)                # P_ij (0 where masked)
+            o = p @ vh[c_lo:c_hi]                               # O_i
+            delta = np.sum(doh[rows] * o, axis=1)               # delta_i = <dO_i, O_i>
+            pc = np.zeros((rows.size, cols.size))
+            pc[:, inside] = p[:, cols[inside] - c_lo]           # P at the requested keys
+            dpc = doh[rows] @ vh[cols].T                        # dP_ij = <dO_i, V_j>
+            dsc = pc * (dpc - delta[:, None])                   # dS_ij = P_ij (dP_ij - delta_i)
+            dK += scale * (dsc.T @ qh[rows])                    # dK_j = s sum_i dS_ij Q_i
+            dV += pc.T @ doh[rows]                              # dV_j = sum_i P_ij dO_i
+        if progress is not None:
+            progress(n + 1, n_blocks)
     return dK, dV

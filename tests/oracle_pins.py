@@ -366,6 +366,18 @@ def pin_row_and_column_helpers(A):
         dk, dv = A.cols_dkdv(q, k, v, do, 1, 1, cols, True, window, 0.4, row_block=7)
         assert np.max(np.abs(dk - r["dK"][1, 1, cols])) <= 1e-13
         assert np.max(np.abs(dv - r["dV"][1, 1, cols])) <= 1e-13
+    # the column helper with sink keys, fewer queries than keys, packed documents and no mask
+    qc, kc, vc, dc = _rng_inputs(30, 1, 4, 2, 37, 8, Sk=60)
+    cu = np.array([[0, 9, 9, 31, 60]])
+    for qq, dd, causal, window, sink, docs in ((q, do, True, 9, 3, None), (qc, dc, True, 13, 2, None),
+                                               (qc, dc, False, 0, 0, None), (q[:1], do[:1], True, 0, 0, cu)):
+        kk, vv = (kc, vc) if qq is qc else (k[:qq.shape[0]], v[:qq.shape[0]])
+        r = A.forward_backward(qq, kk, vv, dd, causal, window, 0.4, sink=sink, cu_seqlens=docs)
+        cols = np.array([0, 2, 8, 9, 30, 31, 59])
+        dk, dv = A.cols_dkdv(qq, kk, vv, dd, 0, 1, cols, causal, window, 0.4, row_block=5, sink=sink,
+                             cu_seqlens=docs)
+        assert np.max(np.abs(dk - r["dK"][0, 1, cols])) <= 1e-13, (causal, window, sink, docs)
+        assert np.max(np.abs(dv - r["dV"][0, 1, cols])) <= 1e-13, (causal, window, sink, docs)
 
 
 # ---------------------------------------------------------------- fewer queries than keys

@@ -25,7 +25,6 @@ def test_visible_mask_reading():
     assert m[1].sum() == 1024 and m[1, 0] and m[1, 1023]
     assert m[2].sum() == 1024 and not m[2, 0] and m[2, 1] and m[2, 1024]
     assert m[3].sum() == 1024 and m[3, 3977] and not m[3, 3976] and not m[3, 5001]
-    assert A.visible_count(10, 20, False, 0) == 20
     with pytest.raises(ValueError):
         A.forward_backward(*(P._rng_inputs(0, 1, 2, 2, 4, 2)[:3]), None, False, 3, 1.0)
     with pytest.raises(ValueError):
