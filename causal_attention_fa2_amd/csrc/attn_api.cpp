@@ -35,6 +35,8 @@ int check_common(int dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int c
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
   if (!causal && window > 0) return ATTN_ERR_UNSUPPORTED;
+  // the kernels take a row's maximum of the raw scores and scale it afterwards: needs scale > 0
+  if (!(scale > 0.f)) return ATTN_ERR_UNSUPPORTED;
   if (Sq > Sk) return ATTN_ERR_UNSUPPORTED;  // the queries are the last Sq of Sk positions
   const int64_t q_elems = (int64_t)B * Hq * Sq * D, kv_elems = (int64_t)B * Hkv * Sk * D;
   if (q_elems >= ((int64_t)1 << 31) || kv_elems >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;

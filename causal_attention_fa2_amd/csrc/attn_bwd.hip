@@ -11,12 +11,12 @@
 //      log-sum-exp lse_i * log2(e), and stores both for the dK / dV pass; then S^T = K Q^T and
 //      dP^T = V dO^T from LDS key/value tiles, dS^T in registers is the B operand of
 //      dQ^T += K^T dS^T with K^T read through the transposing LDS read.
-//   2. dkdv_kernel (attn_dkdv.hip): each wave owns 32 keys whose K and V rows stay in registers as B operands of
-//      S = Q K^T and dP = dO V^T, so a lane owns one key and its accumulator holds query rows --
-//      exactly the contraction side that dV += P^T dO and dK += dS^T Q need. Query / dO / lse /
-//      delta tiles of the group's heads stream through a 3-stage LDS-DMA ring (two tiles in
-//      flight ahead of the one in use); dK and dV for the
-//      group accumulate in registers. A workgroup takes key tile j and then key tile T-1-j, so
+//   2. dkdv_pair_kernel (bf16) / dkdv_kernel (fp32) (attn_dkdv.hip): the K and V rows of a wave's
+//      32 keys stay in registers as B operands of S = Q K^T and dP = dO V^T, so a lane owns one
+//      key and its accumulator holds query rows -- exactly the contraction side that
+//      dV += P^T dO and dK += dS^T Q need. Query / dO / lse / delta tiles of the group's heads
+//      stream through an LDS-DMA ring (bf16: two stages, one tile in flight ahead of the one in
+//      use; fp32: three); dK and dV for the group accumulate in registers. A workgroup takes key tile j and then key tile T-1-j, so
 //      under the causal mask every workgroup does the same amount of work. When that leaves too
 //      few workgroups to fill the GPU, the head group is split into `hs` parts whose fp32 partial
 //      sums go to the workspace and

@@ -64,7 +64,9 @@ typedef enum {
                                non-finite scale, workspace too small, n_docs <= 0 */
   ATTN_ERR_UNSUPPORTED = 2, /* D not 64 or 128, unknown dtype, window > 0 without causal,
                                Sq > Sk, B*Hq*Sq*D or B*Hkv*Sk*D >= 2^31, a paged block size
-                               that is not a power of two in [16, 2^20], n_docs > 2047 */
+                               that is not a power of two in [16, 2^20], n_docs > 2047,
+                               scale <= 0 (the kernels take each row's maximum of the raw scores
+                               before scaling, which needs scale > 0) */
   ATTN_ERR_DEVICE = 3       /* the HIP runtime reported an error for a launch */
 } attn_status_t;
 
@@ -170,8 +172,9 @@ int attn_decode_fwd(int dtype, const void* q, const void* k, const void* v, cons
 
 /* Optional launch observer, for profiling. When set, every entry point calls
  * hook(kernel, 0, stream, user) just before and hook(kernel, 1, stream, user) just after it
- * enqueues each of its kernels ("attn_fwd", "attn_bwd_delta", "attn_bwd_dkdv",
- * "attn_bwd_dkdv_reduce" (only when the head group is split), "attn_bwd_dq", "attn_decode",
+ * enqueues each of its kernels ("attn_fwd", "attn_bwd_dq" (which also forms the delta rows),
+ * "attn_bwd_dkdv", "attn_bwd_dkdv_reduce" (only when the head group is split),
+ * "attn_bwd_dkdv_chunks" (only when the sink key tile is split), "attn_decode",
  * "attn_decode_combine"),
  * on the calling thread, so the hook can record timing events on `stream` around exactly one
  * kernel. NULL (the default) turns it off. The setting is process-wide; set it while no other

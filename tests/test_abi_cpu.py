@@ -182,6 +182,10 @@ def test_fwd_validation(lib):
     assert fwd(lib, dtype=7) == UNS
     assert fwd(lib, causal=0, window=4) == UNS
     assert fwd(lib, B=1, Hq=64, Hkv=8, S=262144, D=128) == UNS  # 2^31 elements
+    # the kernels scale each row's maximum of the raw scores: a scale <= 0 is refused
+    assert fwd(lib, scale=0.0) == UNS
+    assert fwd(lib, scale=-0.125) == UNS
+    assert fwd(lib, scale=float("-inf")) == INV
 
 
 def test_bwd_validation(lib):
@@ -195,6 +199,8 @@ def test_bwd_validation(lib):
     assert bwd(lib, need, Hq=4, Hkv=3) == INV
     assert bwd(lib, need, D=32) == UNS
     assert bwd(lib, need, causal=0, window=1) == UNS
+    assert bwd(lib, need, scale=0.0) == UNS
+    assert bwd(lib, need, scale=-0.125) == UNS
 
 
 def fwd_qk(lib, dtype=1, ptrs=(P, P, P, P, P), B=1, Hq=2, Hkv=2, Sq=16, Sk=64, D=64, causal=1,
