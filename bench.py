@@ -71,9 +71,10 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE summaries, if they
-    were taken on the current kernel source; otherwise None."""
+def load_profile(kernel: str, workload: str):
+    """The committed rocprofv3 counter summary of one kernel on one workload (HBM bytes per launch
+    from FETCH_SIZE / WRITE_SIZE, MFMA busy fraction and executed MFMA instructions from the SQ
+    counters), if it was taken on the current kernel source; otherwise None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -82,7 +83,13 @@ def load_traffic(kernel: str, workload: str):
     rec = data.get(f"{kernel}@{workload}")
     if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the profile summary (None if absent or stale)."""
+    rec = load_profile(kernel, workload)
+    return None if rec is None else rec.get("bytes_per_launch")
 
 
 def device_peak_bf16(torch):
@@ -409,6 +416,13 @@ def main() -> int:
             rec["tflops"] = round(fl[name] / (t * 1e-3) / 1e12, 1)
         elif name in hbm_bytes:
             rec["gbs"] = round(hbm_bytes[name] / (t * 1e-3) / 1e9, 1)
+        prof = load_profile(name, w.name)  # counters taken on this kernel source, else absent
+        if prof is not None:
+            for key in ("mfma_busy", "mfma_insts_per_launch", "bytes_per_launch"):
+                if prof.get(key) is not None:
+                    rec[key] = prof[key]
+            if prof.get("bytes_per_launch"):
+                rec["hbm_gbs"] = round(prof["bytes_per_launch"] / (t * 1e-3) / 1e9, 1)
         kernels[name] = rec
     dom = max(kern_ms, key=kern_ms.get)
     if dom in fl:
@@ -420,6 +434,8 @@ def main() -> int:
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4)}
     roof["traffic"] = load_traffic(dom, w.name)
+    prof = load_profile(dom, w.name)
+    roof["mfma_busy"] = None if prof is None else prof.get("mfma_busy")
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1,
