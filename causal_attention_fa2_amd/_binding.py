@@ -13,7 +13,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
 
-ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_DEVICE = 0, 1, 2, 3
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_DEVICE, ATTN_ERR_SCRATCH = 0, 1, 2, 3, 4
+ATTN_NOALLOC_SCRATCH_BYTES = 72 << 20  # size of attn_bwd_qk_noalloc's static scratch array
 ATTN_F32, ATTN_BF16 = 0, 1
 
 _lib = None
@@ -51,6 +52,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_bwd_qk.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                 i, i, i, i, i, i, i, i, i, f, vp]
     lib.attn_bwd_qk.restype = i
+    lib.attn_bwd_qk_noalloc.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        i, i, i, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd_qk_noalloc.restype = i
     lib.attn_bwd_qk_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.attn_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_qk_workspace_bytes_for.argtypes = [i, i, i, i, i, i, i, i, i]
@@ -295,6 +299,8 @@ def attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, wi
 
 
 def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scale):
+    """Checks the tensors and returns (pointers, sizes, mask arguments); workspace=None leaves the
+    workspace pointer and size out of the pointers."""
     import torch
     if not q.is_contiguous() or q.device.type != "cuda":
         raise ValueError("q must be a contiguous GPU tensor")
@@ -306,12 +312,13 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, window, scal
                          ("dv", dv, (B, Hkv, Sk, D))):
         _check_tensor(name, t, shp, q.dtype, q.device)
     _check_tensor("lse", lse, (B, Hq, Sq), torch.float32, q.device)
-    if workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on q's device")
     scale = D ** -0.5 if scale is None else float(scale)
-    nbytes = workspace.numel() * workspace.element_size()
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), nbytes)
+            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    if workspace is not None:
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ptrs += (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     return ptrs, (B, Hq, Hkv, Sq, Sk, D), (int(bool(causal)), int(window), scale)
 
 
@@ -338,6 +345,19 @@ def attn_bwd_qk(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = Tru
                                     _stream(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_qk")
+
+
+def attn_bwd_qk_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal: bool = True, window: int = 0,
+                        scale: float | None = None, stream=None, sink: int = 0) -> None:
+    """Calls attn_bwd_qk_noalloc: attn_bwd_qk without a workspace argument (the library's static
+    per-device scratch array serves instead; nothing is allocated). Raises AttnError with status
+    ATTN_ERR_SCRATCH when the problem needs more than ATTN_NOALLOC_SCRATCH_BYTES."""
+    ptrs, (B, Hq, Hkv, Sq, Sk, D), (c, w, sc) = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, None,
+                                                          causal, window, scale)
+    st = load_library().attn_bwd_qk_noalloc(_dtype_code(q), *ptrs, B, Hq, Hkv, Sq, Sk, D, c, w,
+                                            int(sink), sc, _stream(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_qk_noalloc")
 
 
 # ---------------------------------------------------------------- allocation conveniences

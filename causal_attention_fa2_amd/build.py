@@ -21,6 +21,7 @@ SOURCES = [
     ("attn_bwd.hip", []),
     ("attn_dkdv.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("attn_decode.hip", []),
+    ("attn_noalloc.hip", []),
 ]
 
 HIPCC_FLAGS = [

@@ -25,8 +25,11 @@ namespace {
 attn_launch_hook_t g_hook = nullptr;
 void* g_hook_user = nullptr;
 
-int check_common(int dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
-                 int window, int sink, float scale) {
+}  // namespace
+
+namespace fa {
+int check_args(int dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window,
+               int sink, float scale) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || D <= 0) return ATTN_ERR_INVALID;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
   if (window < 0 || sink < 0) return ATTN_ERR_INVALID;
@@ -43,9 +46,6 @@ int check_common(int dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int c
   return ATTN_OK;
 }
 
-}  // namespace
-
-namespace fa {
 void notify_launch(const char* kernel, int after, void* stream) {
   attn_launch_hook_t h = g_hook;
   if (h) h(kernel, after, stream, g_hook_user);
@@ -64,7 +64,7 @@ int attn_fwd_qk(int dtype, const void* q, const void* k, const void* v, void* o,
                 int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, int sink,
                 float scale, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
-  int st = check_common(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, scale);
+  int st = fa::check_args(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, scale);
   if (st != ATTN_OK) return st;
   fa::Args a{};
   a.dtype = dtype;
@@ -93,13 +93,13 @@ int attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, fl
 }
 
 size_t attn_bwd_qk_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
-  if (check_common(ATTN_BF16, B, Hq, Hkv, Sq, Sk, D, 1, 0, 0, 1.0f) != ATTN_OK) return 0;
+  if (fa::check_args(ATTN_BF16, B, Hq, Hkv, Sq, Sk, D, 1, 0, 0, 1.0f) != ATTN_OK) return 0;
   return fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D);
 }
 
 size_t attn_bwd_qk_workspace_bytes_for(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
                                        int window, int sink) {
-  if (check_common(ATTN_BF16, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, 1.0f) != ATTN_OK) return 0;
+  if (fa::check_args(ATTN_BF16, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, 1.0f) != ATTN_OK) return 0;
   return fa::bwd_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, causal, window, sink);
 }
 
@@ -113,7 +113,7 @@ int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const vo
                 int window, int sink, float scale, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return ATTN_ERR_INVALID;
-  int st = check_common(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, scale);
+  int st = fa::check_args(dtype, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, scale);
   if (st != ATTN_OK) return st;
   if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)) return ATTN_ERR_INVALID;
   fa::Args a{};
@@ -169,7 +169,7 @@ int attn_fwd_paged(int dtype, const void* q, const void* k_pool, const void* v_p
   const int64_t capacity = (int64_t)max_blocks * block_size;  // keys one sequence can hold
   if (capacity >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   // Sk = Sq here only for the shared checks; each sequence's own Sk comes from seqlen_k
-  int st = check_common(dtype, B, Hq, Hkv, Sq, Sq, D, causal, window, sink, scale);
+  int st = fa::check_args(dtype, B, Hq, Hkv, Sq, Sq, D, causal, window, sink, scale);
   if (st != ATTN_OK) return st;
   if (Sq > capacity) return ATTN_ERR_UNSUPPORTED;
   fa::Args a{};
@@ -205,7 +205,7 @@ int attn_fwd_varlen(int dtype, const void* q, const void* k, const void* v, void
   if (!q || !k || !v || !o || !lse || !cu_seqlens) return ATTN_ERR_INVALID;
   if (n_docs <= 0) return ATTN_ERR_INVALID;
   if (n_docs > fa::kMaxDocs) return ATTN_ERR_UNSUPPORTED;
-  int st = check_common(dtype, B, Hq, Hkv, S, S, D, 1, window, 0, scale);
+  int st = fa::check_args(dtype, B, Hq, Hkv, S, S, D, 1, window, 0, scale);
   if (st != ATTN_OK) return st;
   fa::Args a{};
   a.dtype = dtype;
@@ -237,7 +237,7 @@ int attn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, cons
     return ATTN_ERR_INVALID;
   if (n_docs <= 0) return ATTN_ERR_INVALID;
   if (n_docs > fa::kMaxDocs) return ATTN_ERR_UNSUPPORTED;
-  int st = check_common(dtype, B, Hq, Hkv, S, S, D, 1, window, 0, scale);
+  int st = fa::check_args(dtype, B, Hq, Hkv, S, S, D, 1, window, 0, scale);
   if (st != ATTN_OK) return st;
   if (workspace_bytes < fa::bwd_workspace_bytes(B, Hq, Hkv, S, S, D)) return ATTN_ERR_INVALID;
   fa::Args a{};
@@ -271,7 +271,7 @@ int attn_bwd_varlen(int dtype, const void* q, const void* k, const void* v, cons
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int max_keys, int D) {
-  if (check_common(ATTN_BF16, B, Hq, Hkv, Sq, max_keys, D, 1, 0, 0, 1.0f) != ATTN_OK) return 0;
+  if (fa::check_args(ATTN_BF16, B, Hq, Hkv, Sq, max_keys, D, 1, 0, 0, 1.0f) != ATTN_OK) return 0;
   if ((Hq / Hkv) * Sq > 32) return 0;
   return fa::decode_workspace_bytes(B, Hq, Hkv, Sq, max_keys, D);
 }
@@ -300,7 +300,7 @@ int attn_decode_fwd(int dtype, const void* q, const void* k, const void* v, cons
     a.pg.max_blocks = max_blocks;
     a.pg.num_blocks = num_blocks;
   }
-  int st = check_common(dtype, B, Hq, Hkv, Sq, max_keys, D, causal, window, sink, scale);
+  int st = fa::check_args(dtype, B, Hq, Hkv, Sq, max_keys, D, causal, window, sink, scale);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16 || (Hq / Hkv) * Sq > 32) return ATTN_ERR_UNSUPPORTED;
   if (workspace_bytes < fa::decode_workspace_bytes(B, Hq, Hkv, Sq, max_keys, D)) return ATTN_ERR_INVALID;
@@ -331,6 +331,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_INVALID: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case ATTN_ERR_DEVICE: return "HIP runtime error at launch";
+    case ATTN_ERR_SCRATCH: return "problem needs more than the static scratch buffer holds";
     default: return "unknown status";
   }
 }

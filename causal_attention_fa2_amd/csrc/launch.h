@@ -53,6 +53,11 @@ struct Args {
   Docs docs;   // packed documents (Sq = Sk, causal, no sinks)
 };
 
+// The argument checks every entry point shares: ATTN_OK (0) or the attn_status_t of the first
+// failed check (sizes, head grouping, mask arguments, dtype, head dimension, scale).
+int check_args(int dtype, int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window,
+               int sink, float scale);
+
 // Tells the launch observer (attn_set_launch_hook) that `kernel` is about to be / has been
 // enqueued on `stream`.
 void notify_launch(const char* kernel, int after, void* stream);

@@ -39,7 +39,8 @@
  * All are dense and contiguous with D fastest, element type `dtype` (lse is always float32).
  *
  * Ownership and execution: every pointer is a DEVICE pointer owned by the caller. The library
- * never allocates, never synchronises the host, keeps no per-call state, and enqueues all of its
+ * never allocates (its one static array, attn_bwd_qk_noalloc's scratch, is placed by the HIP
+ * runtime on each device where the library's code is loaded), never synchronises the host, keeps no per-call state, and enqueues all of its
  * work on `stream` (a hipStream_t; NULL = the default stream). Outputs must not alias inputs.
  * Calls on different streams may run concurrently; results are deterministic (no atomics).
  *
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 typedef enum {
   ATTN_OK = 0,
@@ -67,7 +68,9 @@ typedef enum {
                                that is not a power of two in [16, 2^20], n_docs > 2047,
                                scale <= 0 (the kernels take each row's maximum of the raw scores
                                before scaling, which needs scale > 0) */
-  ATTN_ERR_DEVICE = 3       /* the HIP runtime reported an error for a launch */
+  ATTN_ERR_DEVICE = 3,      /* the HIP runtime reported an error for a launch */
+  ATTN_ERR_SCRATCH = 4      /* attn_bwd_qk_noalloc: the problem needs more workspace than its
+                               static scratch array holds (ATTN_NOALLOC_SCRATCH_BYTES) */
 } attn_status_t;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
@@ -124,6 +127,21 @@ int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const vo
                 void* workspace, size_t workspace_bytes,
                 int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, int sink,
                 float scale, void* stream);
+
+/* For callers that cannot allocate device memory (code under stream capture, serving loops,
+ * harnesses that forbid hipMalloc): attn_bwd_qk with the same arguments minus the workspace, which
+ * comes from a static device array of ATTN_NOALLOC_SCRATCH_BYTES (one per device, held until the
+ * process ends; enough for B=1, Hq=64, Hkv=8, S=4096, D=128 with its head split). Results are
+ * bitwise those of attn_bwd_qk given a workspace of that size. Returns ATTN_ERR_SCRATCH, before
+ * enqueueing anything, when attn_bwd_qk_workspace_bytes(...) exceeds the array; the sink split is
+ * used only when attn_bwd_qk_workspace_bytes_for(...) fits. Allocates nothing. Every call on one
+ * device uses that device's array (the device of `stream`, or the current device for NULL), so
+ * calls that overlap in time on one device race; nothing needs clearing between calls. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (72u << 20)
+int attn_bwd_qk_noalloc(int dtype, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window,
+                        int sink, float scale, void* stream);
 
 /* Forward against a paged K/V cache. k_pool and v_pool are [num_blocks, Hkv, block_size, D]
  * (dtype); block_table is int32 [B, max_blocks]: logical block t of sequence b (its tokens

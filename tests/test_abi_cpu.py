@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_qk", "attn_bwd_qk_workspace_bytes",
+    assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_qk", "attn_bwd_qk_noalloc",
+                     "attn_bwd_qk_workspace_bytes",
                      "attn_bwd_qk_workspace_bytes_for",
                      "attn_bwd_varlen", "attn_bwd_workspace_bytes", "attn_decode_fwd",
                      "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_paged", "attn_fwd_qk",
@@ -44,11 +45,12 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert fa.attn_abi_version() == 7
+    assert fa.attn_abi_version() == 8
     assert fa.attn_status_string(0) == "ok"
     assert fa.attn_status_string(1) == "invalid argument"
     assert fa.attn_status_string(2) == "unsupported configuration"
     assert fa.attn_status_string(3) == "HIP runtime error at launch"
+    assert fa.attn_status_string(4) == "problem needs more than the static scratch buffer holds"
     assert fa.attn_status_string(99) == "unknown status"
 
 
@@ -241,6 +243,40 @@ def test_qk_validation(lib):
     assert bwd_qk(lib, need, Sq=65) == UNS
     assert bwd_qk(lib, need, window=4, sink=-1) == INV
     assert bwd_qk(lib, need, D=32) == UNS
+
+
+def bwd_noalloc(lib, ptrs=(P,) * 9, B=1, Hq=2, Hkv=2, Sq=16, Sk=64, D=64, causal=1, window=0,
+                scale=0.125, dtype=1, sink=0):
+    return lib.attn_bwd_qk_noalloc(dtype, *ptrs, B, Hq, Hkv, Sq, Sk, D, causal, window, sink, scale,
+                                   None)
+
+
+def test_noalloc_validation(lib):
+    """Argument checks as attn_bwd_qk; a problem whose workspace exceeds the static array is refused
+    with ATTN_ERR_SCRATCH before any HIP call (so this runs without a GPU)."""
+    INV, UNS, SCR = fa.ATTN_ERR_INVALID, fa.ATTN_ERR_UNSUPPORTED, fa.ATTN_ERR_SCRATCH
+    header = open(HEADER).read()
+    assert re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(72u << 20\)", header)
+    assert fa.ATTN_NOALLOC_SCRATCH_BYTES == 72 << 20
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = None
+        assert bwd_noalloc(lib, ptrs=ptrs) == INV
+    assert bwd_noalloc(lib, Sq=65) == UNS
+    assert bwd_noalloc(lib, D=32) == UNS
+    assert bwd_noalloc(lib, scale=0.0) == UNS
+    assert bwd_noalloc(lib, window=4, sink=-1) == INV
+    assert bwd_noalloc(lib, Hq=3) == INV
+    # the S=4096, 64/8-head, D=128 backward fits with its head split (2 MiB rows + 64 MiB partials)
+    assert fa.attn_bwd_qk_workspace_bytes(1, 64, 8, 4096, 4096, 128) == 66 << 20
+    # S=6144 splits the head group too: 2 x 2 x 8 x 6144 x 128 fp32 = 96 MiB of partials
+    big = (1, 64, 8, 6144, 6144, 128)
+    assert fa.attn_bwd_qk_workspace_bytes(*big) > fa.ATTN_NOALLOC_SCRATCH_BYTES
+    assert bwd_noalloc(lib, B=1, Hq=64, Hkv=8, Sq=6144, Sk=6144, D=128) == SCR
+    # row arrays alone beyond the array: 2 x 128 heads x 2^17 rows fp32 = 128 MiB
+    assert bwd_noalloc(lib, B=1, Hq=128, Hkv=128, Sq=1 << 17, Sk=1 << 17, D=64) == SCR
+    # argument errors take precedence over the size check
+    assert bwd_noalloc(lib, B=1, Hq=64, Hkv=8, Sq=6144, Sk=6144, D=96) == UNS
 
 
 def fwd_paged(lib, dtype=1, ptrs=(P,) * 7, B=2, Hq=4, Hkv=2, Sq=1, D=128, bs=16, max_blocks=8,
