@@ -9,6 +9,10 @@
 #include "device.h"
 #include "launch.h"
 
+#ifndef ATTN_DKDV_LAG
+#define ATTN_DKDV_LAG 1
+#endif
+
 namespace fa {
 
 template <class E, int D, int NW, int QB, bool VL>
@@ -284,12 +288,14 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
 //   wave w     (S role):  S = Q K^T, P = exp2(S * scale * log2 e - lse * log2 e), dV += P^T dO
 //   wave w + 4 (dP role): dP = dO V^T, dS = P o (dP - delta), dK += dS^T Q
 // P passes from the S wave to its partner through LDS as bf16 in accumulator layout (2 KB per
-// 32 x 32 block). Each step (one 64-row query tile) has two workgroup barriers: the ring barrier
-// (the tile has landed; every wave is done with the previous step, including its P blocks) and one
-// after the products S and dP (the P blocks are written). Around the second barrier each wave's
-// vector work (exponentials, dS) can run while its partner issues matrix products on the shared
-// SIMD. Per wave: its K or V fragments (B operand), its dV or dK accumulators and the two blocks'
-// S / dP accumulators -- the two roles' state shares the same registers.
+// 32 x 32 block). At D = 128 the dP wave runs one query tile behind the S wave (three ring stages,
+// two P buffers), so one workgroup barrier per tile orders both the ring and the P exchange, and
+// within a tile the two waves of a SIMD share no data: the S wave's exponentials can run beside
+// the dP wave's products and the other way round (1.5-5% faster than the two-barrier schedule).
+// At D = 64 (128-row tiles) that does not fit in LDS: two stages, one P buffer and a second
+// barrier after the products S and dP. Per wave: its K or V fragments (B operand), its dV or dK
+// accumulators and the two blocks' S / dP accumulators -- the two roles' state shares the same
+// registers.
 template <int D, int QB, bool VL>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -310,11 +316,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   static_assert(BR % 64 == 0 && 2 * (BR / 64) <= NW, "one row copy (64 floats) per wave");
   constexpr int kRowOff = 2 * QTile::kBytes;  // lse[BR] then delta[BR] (fp32)
   constexpr int kRowWaves = 2 * (BR / 64);      // waves that copy 64 of those floats per tile
-  constexpr int kStage = kRowOff + 8 * BR;
+  constexpr int kStage = (kRowOff + 8 * BR + 1023) / 1024 * 1024;  // one ring stage, 1 KB aligned
   constexpr int kPBlock = 2048;  // one 32 x 32 bf16 P block, 32 bytes per lane
-  __shared__ __attribute__((aligned(1024))) char st0[kStage];
-  __shared__ __attribute__((aligned(1024))) char st1[kStage];
-  __shared__ __attribute__((aligned(1024))) char pbuf[NP * QB * kPBlock];
+  constexpr int kPBuf = NP * QB * kPBlock;
+  constexpr int kExtra = VL ? 4 * (kMaxDocs + 1) + 8 * kBalancedTiles : 0;
+  // Lagged schedule (when three stages and two P buffers fit in LDS): the dP-role wave works on
+  // the query tile before the S-role wave's, so one barrier per step orders both the ring and the
+  // P exchange. Otherwise two stages, one P buffer and a second barrier inside each step.
+  constexpr bool kLag = ATTN_DKDV_LAG != 0 && 3 * kStage + 2 * kPBuf + kExtra <= 160 * 1024;
+  constexpr int kNStage = kLag ? 3 : 2;
+  __shared__ __attribute__((aligned(1024))) char ring[kNStage * kStage];
+  __shared__ __attribute__((aligned(1024))) char pbuf[(kLag ? 2 : 1) * kPBuf];
   __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
   __shared__ int tile_cost[VL ? kBalancedTiles : 1];
   __shared__ int tile_order[VL ? kBalancedTiles : 1];
@@ -473,7 +485,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     // One 64-row (128 for D = 64) query tile. Blocks of 32 rows that see none of this pair's keys
     // (the causal diagonal, window edges) are computed like partial ones: every P is 0, so they
     // add exact zeros to dV and dK.
-    auto compute = [&](int it, const char* q_lds) __attribute__((always_inline)) {
+    auto compute = [&](int it, const char* q_lds, char* ps) __attribute__((always_inline)) {
       const char* do_lds = q_lds + QTile::kBytes;
       const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
       const float* dl_lds = lse_lds + BR;
@@ -513,16 +525,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
           }
 #pragma unroll
           for (int t = 0; t < 2; ++t)
-            *reinterpret_cast<u32x4_t*>(pslot + qb * kPBlock + t * 1024) = acc_frag<E>(xs[qb], t).v;
+            *reinterpret_cast<u32x4_t*>(ps + qb * kPBlock + t * 1024) = acc_frag<E>(xs[qb], t).v;
         }
       }
-      barrier_keep_vm();  // the P blocks are in LDS
+      if constexpr (!kLag) barrier_keep_vm();  // the P blocks are in LDS
       // Phase 2: dV += P^T dO (S role); dS = P o (dP - delta), dK += dS^T Q (dP role).
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if constexpr (!SR) {
-          const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(pslot + qb * kPBlock);
-          const u32x4_t pb = *reinterpret_cast<const u32x4_t*>(pslot + qb * kPBlock + 1024);
+          const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(ps + qb * kPBlock);
+          const u32x4_t pb = *reinterpret_cast<const u32x4_t*>(ps + qb * kPBlock + 1024);
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int rb = 32 * qb + 8 * r4 + 4 * half;
@@ -549,21 +561,48 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     };
 
     int ch, ct, ih, iq;
-    // Two-stage ring (one tile in flight): step s waits for its own tile, then, once every wave is
-    // past step s - 1, copies tile s + 1 into the stage step s - 1 used. 2-4% faster than three
-    // stages with two tiles in flight, on every workload measured.
+    // Unlagged: two-stage ring (one tile in flight): step s waits for its own tile, then, once
+    // every wave is past step s - 1, copies tile s + 1 into the stage step s - 1 used (2-4% faster
+    // than three stages with two tiles in flight).
     auto step = [&](auto stc, int s) __attribute__((always_inline)) {
       constexpr int ST = decltype(stc)::value;
-      char* cur = ST == 0 ? st0 : st1;
-      char* nn = ST == 0 ? st1 : st0;
       wait_vmcnt<0>();
       barrier_keep_vm();
       if (s + 1 < n_steps) {
-        issue(ih, iq, nn);
+        issue(ih, iq, ring + (1 - ST) * kStage);
         advance(ih, iq);
       }
-      compute(ct, cur);
+      compute(ct, ring + ST * kStage, pslot);
       advance(ch, ct);
+    };
+    // Lagged: interval k (after its one barrier) copies tile k + 1 into the stage tile k - 2 used,
+    // while the S wave takes step k (tile k % 3, P buffer k % 2) and the dP wave step k - 1, whose P
+    // the barrier has just published. Tile k - 2's last reader ran in interval k - 1, and so did the
+    // last reader of P buffer k % 2.
+    auto lagged = [&]() __attribute__((always_inline)) {
+      int sc = 0;  // stage of tile k
+      for (int k = 0; k <= n_steps; ++k) {
+        const int sn = sc == 2 ? 0 : sc + 1;  // stage of tile k + 1
+        const int sp = sc == 0 ? 2 : sc - 1;  // stage of tile k - 1
+        wait_vmcnt<0>();
+        barrier_keep_vm();
+        if (k + 1 < n_steps) {
+          issue(ih, iq, ring + sn * kStage);
+          advance(ih, iq);
+        }
+        if constexpr (SR) {
+          if (k < n_steps) {
+            compute(ct, ring + sc * kStage, pslot + (k & 1) * kPBuf);
+            advance(ch, ct);
+          }
+        } else {
+          if (k > 0) {
+            compute(ct, ring + sp * kStage, pslot + ((k - 1) & 1) * kPBuf);
+            advance(ch, ct);
+          }
+        }
+        sc = sn;
+      }
     };
     const int n_seg = two ? 2 : 1;
     for (int seg = 0; seg < n_seg; ++seg) {
@@ -572,13 +611,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
       load_kv();
       ch = 0, ct = 0, ih = 0, iq = 0;
       if (n_steps > 0) {
-        issue(ih, iq, st0);
+        issue(ih, iq, ring);
         advance(ih, iq);
       }
-      wait_vmcnt<0>();
-      for (int s = 0; s < n_steps; s += 2) {
-        step(IC<0>{}, s);
-        if (s + 1 < n_steps) step(IC<1>{}, s + 1);
+      if constexpr (kLag) {
+        if (n_steps > 0) lagged();
+      } else {
+        wait_vmcnt<0>();
+        for (int s = 0; s < n_steps; s += 2) {
+          step(IC<0>{}, s);
+          if (s + 1 < n_steps) step(IC<1>{}, s + 1);
+        }
       }
       flush();
     }
