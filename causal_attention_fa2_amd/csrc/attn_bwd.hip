@@ -15,8 +15,9 @@
 //      32 keys stay in registers as B operands of S = Q K^T and dP = dO V^T, so a lane owns one
 //      key and its accumulator holds query rows -- exactly the contraction side that
 //      dV += P^T dO and dK += dS^T Q need. Query / dO / lse / delta tiles of the group's heads
-//      stream through an LDS-DMA ring (bf16: two stages, one tile in flight ahead of the one in
-//      use; fp32: three); dK and dV for the group accumulate in registers. A workgroup takes key tile j and then key tile T-1-j, so
+//      stream through an LDS-DMA ring with one tile in flight (bf16 at D = 128: three stages,
+//      the dP wave one tile behind the S wave; bf16 at D = 64: two; fp32: three stages, two in
+//      flight); dK and dV for the group accumulate in registers. A workgroup takes key tile j and then key tile T-1-j, so
 //      under the causal mask every workgroup does the same amount of work. When that leaves too
 //      few workgroups to fill the GPU, the head group is split into `hs` parts whose fp32 partial
 //      sums go to the workspace and
@@ -153,11 +154,20 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16_t st = f32x16_t{}, dpt = f32x16_t{};
+      // all K fragments of the key block are requested before its S products (one LDS latency),
+      // the V fragments under those products
+      Frag<E> kfr[DS];
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) kfr[s2] = RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s2);
+      __builtin_amdgcn_sched_barrier(0);
+      Frag<E> vfr[DS];
 #pragma unroll
       for (int s2 = 0; s2 < DS; ++s2) {
-        mma(st, RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s2), qf[s2]);
-        mma(dpt, RowFrag<E, KvTile>::get(v_lds, 32 * kb + l32, s2), df[s2]);
+        vfr[s2] = RowFrag<E, KvTile>::get(v_lds, 32 * kb + l32, s2);
+        mma(st, kfr[s2], qf[s2]);
       }
+#pragma unroll
+      for (int s2 = 0; s2 < DS; ++s2) mma(dpt, vfr[s2], df[s2]);
       // P = exp2(S * scale * log2 e - lse * log2 e), masked to 0 in place on partial tiles (one
       // code path, so no register copies where masked and unmasked tiles rejoin), then
       // dS = P o (dP - delta).
