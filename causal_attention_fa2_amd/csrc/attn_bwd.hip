@@ -15,9 +15,8 @@
 //      32 keys stay in registers as B operands of S = Q K^T and dP = dO V^T, so a lane owns one
 //      key and its accumulator holds query rows -- exactly the contraction side that
 //      dV += P^T dO and dK += dS^T Q need. Query / dO / lse / delta tiles of the group's heads
-//      stream through an LDS-DMA ring with one tile in flight (bf16 at D = 128: three stages,
-//      the dP wave one tile behind the S wave; bf16 at D = 64: two; fp32: three stages, two in
-//      flight); dK and dV for the group accumulate in registers. A workgroup takes key tile j and then key tile T-1-j, so
+//      stream through an LDS-DMA ring (bf16: three stages with one tile in flight, the dP wave one
+//      tile behind the S wave; fp32: three stages, two in flight); dK and dV for the group accumulate in registers. A workgroup takes key tile j and then key tile T-1-j, so
 //      under the causal mask every workgroup does the same amount of work. When that leaves too
 //      few workgroups to fill the GPU, the head group is split into `hs` parts whose fp32 partial
 //      sums go to the workspace and

@@ -9,10 +9,6 @@
 #include "device.h"
 #include "launch.h"
 
-#ifndef ATTN_DKDV_LAG
-#define ATTN_DKDV_LAG 1
-#endif
-
 namespace fa {
 
 template <class E, int D, int NW, int QB, bool VL>
@@ -288,14 +284,13 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
 //   wave w     (S role):  S = Q K^T, P = exp2(S * scale * log2 e - lse * log2 e), dV += P^T dO
 //   wave w + 4 (dP role): dP = dO V^T, dS = P o (dP - delta), dK += dS^T Q
 // P passes from the S wave to its partner through LDS as bf16 in accumulator layout (2 KB per
-// 32 x 32 block). At D = 128 the dP wave runs one query tile behind the S wave (three ring stages,
-// two P buffers), so one workgroup barrier per tile orders both the ring and the P exchange, and
-// within a tile the two waves of a SIMD share no data: the S wave's exponentials can run beside
-// the dP wave's products and the other way round (1.5-5% faster than the two-barrier schedule).
-// At D = 64 (128-row tiles) that does not fit in LDS: two stages, one P buffer and a second
-// barrier after the products S and dP. Per wave: its K or V fragments (B operand), its dV or dK
-// accumulators and the two blocks' S / dP accumulators -- the two roles' state shares the same
-// registers.
+// 32 x 32 block). The dP wave runs one query tile behind the S wave (three ring stages, two P
+// buffers), so one workgroup barrier per tile orders both the ring and the P exchange, and within
+// a tile the two waves of a SIMD share no data: the S wave's exponentials can run beside the dP
+// wave's products and the other way round (1.5-5% faster than a schedule with a second barrier
+// between the products S / dP and the P exchange). Per wave: its K or V fragments (B operand), its
+// dV or dK accumulators and the two blocks' S / dP accumulators -- the two roles' state shares the
+// same registers.
 template <int D, int QB, bool VL>
 __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -320,13 +315,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   constexpr int kPBlock = 2048;  // one 32 x 32 bf16 P block, 32 bytes per lane
   constexpr int kPBuf = NP * QB * kPBlock;
   constexpr int kExtra = VL ? 4 * (kMaxDocs + 1) + 8 * kBalancedTiles : 0;
-  // Lagged schedule (when three stages and two P buffers fit in LDS): the dP-role wave works on
-  // the query tile before the S-role wave's, so one barrier per step orders both the ring and the
-  // P exchange. Otherwise two stages, one P buffer and a second barrier inside each step.
-  constexpr bool kLag = ATTN_DKDV_LAG != 0 && 3 * kStage + 2 * kPBuf + kExtra <= 160 * 1024;
-  constexpr int kNStage = kLag ? 3 : 2;
-  __shared__ __attribute__((aligned(1024))) char ring[kNStage * kStage];
-  __shared__ __attribute__((aligned(1024))) char pbuf[(kLag ? 2 : 1) * kPBuf];
+  // Lagged schedule: the dP-role wave works on the query tile before the S-role wave's, so one
+  // barrier per step orders both the ring (three stages) and the P exchange (two buffers).
+  static_assert(3 * kStage + 2 * kPBuf + kExtra <= 160 * 1024, "three stages and two P buffers fit in LDS");
+  __shared__ __attribute__((aligned(1024))) char ring[3 * kStage];
+  __shared__ __attribute__((aligned(1024))) char pbuf[2 * kPBuf];
   __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
   __shared__ int tile_cost[VL ? kBalancedTiles : 1];
   __shared__ int tile_order[VL ? kBalancedTiles : 1];
@@ -482,7 +475,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
       }
     };
 
-    // One 64-row (128 for D = 64) query tile. Blocks of 32 rows that see none of this pair's keys
+    // One 64-row query tile. Blocks of 32 rows that see none of this pair's keys
     // (the causal diagonal, window edges) are computed like partial ones: every P is 0, so they
     // add exact zeros to dV and dK.
     auto compute = [&](int it, const char* q_lds, char* ps) __attribute__((always_inline)) {
@@ -528,7 +521,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
             *reinterpret_cast<u32x4_t*>(ps + qb * kPBlock + t * 1024) = acc_frag<E>(xs[qb], t).v;
         }
       }
-      if constexpr (!kLag) barrier_keep_vm();  // the P blocks are in LDS
       // Phase 2: dV += P^T dO (S role); dS = P o (dP - delta), dK += dS^T Q (dP role).
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -561,20 +553,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     };
 
     int ch, ct, ih, iq;
-    // Unlagged: two-stage ring (one tile in flight): step s waits for its own tile, then, once
-    // every wave is past step s - 1, copies tile s + 1 into the stage step s - 1 used (2-4% faster
-    // than three stages with two tiles in flight).
-    auto step = [&](auto stc, int s) __attribute__((always_inline)) {
-      constexpr int ST = decltype(stc)::value;
-      wait_vmcnt<0>();
-      barrier_keep_vm();
-      if (s + 1 < n_steps) {
-        issue(ih, iq, ring + (1 - ST) * kStage);
-        advance(ih, iq);
-      }
-      compute(ct, ring + ST * kStage, pslot);
-      advance(ch, ct);
-    };
     // Lagged: interval k (after its one barrier) copies tile k + 1 into the stage tile k - 2 used,
     // while the S wave takes step k (tile k % 3, P buffer k % 2) and the dP wave step k - 1, whose P
     // the barrier has just published. Tile k - 2's last reader ran in interval k - 1, and so did the
@@ -614,15 +592,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
         issue(ih, iq, ring);
         advance(ih, iq);
       }
-      if constexpr (kLag) {
-        if (n_steps > 0) lagged();
-      } else {
-        wait_vmcnt<0>();
-        for (int s = 0; s < n_steps; s += 2) {
-          step(IC<0>{}, s);
-          if (s + 1 < n_steps) step(IC<1>{}, s + 1);
-        }
-      }
+      if (n_steps > 0) lagged();
       flush();
     }
   };

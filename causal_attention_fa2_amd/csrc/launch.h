@@ -136,9 +136,10 @@ inline DkdvPlan dkdv_plan(int B, int Hq, int Hkv, int Sk) {
 // tile 0's workgroup, chunks 1.. become small extra workgroups that fill in behind the ordinary
 // ones. Every chunk writes fp32 partial sums of tile 0's dK and dV (per head part) that a small
 // reduce adds in a fixed order.
-// Query rows per streamed tile of the bf16 dK/dV pass: 64, or 128 for D = 64 (half the products
-// per row, so a taller tile per step; 6-9% faster there).
-constexpr int dkdv_query_rows(int D) { return D == 64 ? 128 : 64; }
+// Query rows per streamed tile of the bf16 dK/dV pass: 64 for both head sizes (with the lagged
+// schedule's three stages and two P buffers, 128-row tiles at D = 64 would need 163 KB of LDS;
+// 64-row tiles with the lag beat 128-row tiles with two barriers per step by 1-4%).
+constexpr int dkdv_query_rows(int) { return 64; }
 constexpr int kDkdvMaxChunks = 64;
 constexpr int kComputeUnits = 256;  // MI355X
 inline void dkdv_sink_split(DkdvPlan& p, int B, int Hq, int Hkv, int Sq, int Sk, int D, int window, int sink,

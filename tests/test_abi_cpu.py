@@ -95,14 +95,14 @@ def test_qk_workspace_bytes(lib):
 
 
 def _sink_chunks(B, Hq, Hkv, Sq, Sk, D, window, sink):
-    """Chunks of key tile 0's query range in the sink split (query tiles of 64 rows, 128 for
-    D = 64; 1 = no split):
+    """Chunks of key tile 0's query range in the sink split (query tiles of 64 rows; 1 = no
+    split):
     only when tile 0's workgroup (its range plus an ordinary tile's, times the heads of a part)
     would exceed 1.1x a compute unit's share of the work (256 units); chunks of a quarter of an
     ordinary tile's range, at most 64 of them."""
     if window <= 0 or sink <= 0 or sink > 128:
         return 1
-    off, c1, br = Sk - Sq, min(128, Sk) - 1, 128 if D == 64 else 64
+    off, c1, br = Sk - Sq, min(128, Sk) - 1, 64
 
     def rng(s):  # query tiles holding a row that sees some key in [0, c1] (causal)
         lo = max(0, off) - off
