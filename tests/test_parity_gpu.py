@@ -154,8 +154,8 @@ def test_long_context_workload_sampled():
 def test_long_context_early_key_columns():
     """The same workload: dK / dV of the first keys, element by element. Key tile 0 sums its
     gradient over every query tile of all 8 heads of a group (the longest fp32 accumulation of the
-    pass); keys 0, 1, 127, 128 (key tiles 0 and 1), 4095 and 16384 of KV head 0. The oracle needs
-    every query row here (a whole group's softmax over 32768 keys)."""
+    pass); keys 0, 1, 127, 128 (key tiles 0 and 1), 4095 and 16384 of KV heads 0 and 5. The oracle
+    needs every query row here (a whole group's softmax over 32768 keys)."""
     w = WORKLOADS["gqa64x8-s32768-d128"]
     say("long-context early keys: generating inputs")
     q, k, v, do = make_inputs(w)
@@ -163,9 +163,10 @@ def test_long_context_early_key_columns():
     got = run_hip(q, k, v, do, w.dtype, w.causal, w.window, w.scale)
     cols = np.array([0, 1, 127, 128, 4095, 16384])
 
-    def progress(done, total):
-        if done % 16 == 0 or done == total:
-            say(f"  oracle: {done}/{total} row blocks")
-    dk, dv = oracle.cols_dkdv(q, k, v, do, 0, 0, cols, w.causal, w.window, w.scale, progress=progress)
-    assert_parity({"dK": got["dK"][0, 0, cols], "dV": got["dV"][0, 0, cols]}, {"dK": dk, "dV": dv},
-                  w.dtype, tag=w.name + " (keys 0..16384 of KV head 0)")
+    for g in (0, 5):
+        def progress(done, total):
+            if done % 16 == 0 or done == total:
+                say(f"  oracle, KV head {g}: {done}/{total} row blocks")
+        dk, dv = oracle.cols_dkdv(q, k, v, do, 0, g, cols, w.causal, w.window, w.scale, progress=progress)
+        assert_parity({"dK": got["dK"][0, g, cols], "dV": got["dV"][0, g, cols]}, {"dK": dk, "dV": dv},
+                      w.dtype, tag=w.name + f" (keys 0..16384 of KV head {g})")
