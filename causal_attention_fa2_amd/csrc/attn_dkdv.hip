@@ -433,6 +433,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   // measured); spread between products the step is ≈ 1% shorter. At D = 64 (half the bytes) the
   // spread step was 1-2% slower, so it copies right after the barrier.
   constexpr bool kSpread = D == 128;
+  static_assert(!kSpread || QB == 2, "the two copy halves ride on the two row blocks of a step");
   auto tile_whole = [&](int it) __attribute__((always_inline)) {
     return kSpread && kFast && (lo + nq - 1 - it) * BR + BR <= Sq;
   };
