@@ -133,12 +133,17 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
   const float l2 = LSE[row_idx] * kLog2e;  // base-2 log-sum-exp used by both gradient kernels
   const float nlse2 = -l2;
   if (q_ok && half == 0) {
-    delta[row_idx] = dl;
+    delta[row_idx] = -dl;  // stored negated: the dK / dV pass starts its dP products from it
     LSE2[row_idx] = l2;
   }
   f32x16_t acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
+  // -delta_i in every register: the accumulator the dP products start from, so they leave
+  // dP - delta and dS = P o (dP - delta) takes one multiply per element
+  f32x16_t ndl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl[r] = -dl;
   wait_vmcnt<0>();
 
   auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
     }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      f32x16_t st = f32x16_t{}, dpt = f32x16_t{};
+      f32x16_t st = f32x16_t{}, dpt = ndl;
       // all K fragments of the key block are requested before its S products (one LDS latency),
       // the V fragments under those products
       Frag<E> kfr[DS];
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[r] = st[r] * (dpt[r] - dl);
+      for (int r = 0; r < 16; ++r) st[r] = st[r] * dpt[r];  // dpt holds dP - delta
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const Frag<E> sf = acc_frag<E>(st, t);

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
   static_assert(NW >= 2, "two waves copy lse and delta");
   typedef LdsTile<E, BR, D> QTile;
   constexpr int kTileOps = dma_tile_ops<E, BR, D, NW>();
-  constexpr int kRowOff = 2 * QTile::kBytes;  // lse[64] then delta[64] (fp32)
+  constexpr int kRowOff = 2 * QTile::kBytes;  // lse[64] then -delta[64] (fp32)
   constexpr int kStage = kRowOff + 512;
   __shared__ __attribute__((aligned(1024))) char st0[kStage];
   __shared__ __attribute__((aligned(1024))) char st1[kStage];
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(
               if (!visible(i, my_k, S, causal, window, sink) || (VL && i >= de_lane)) p = 0.f;
             }
             sa[r] = p;
-            dp[r] = p * (dp[r] - dl4[c]);
+            dp[r] = p * (dp[r] + dl4[c]);  // the rows hold -delta
           }
         }
       };
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   constexpr int kTileOps = dma_tile_ops<E, BR, D, NW>();
   static_assert(BR == dkdv_query_rows(D) && BC == 32 * kDkdvWaves, "the host plan assumes these tiles");
   static_assert(BR % 64 == 0 && 2 * (BR / 64) <= NW, "one row copy (64 floats) per wave");
-  constexpr int kRowOff = 2 * QTile::kBytes;  // lse[BR] then delta[BR] (fp32)
+  constexpr int kRowOff = 2 * QTile::kBytes;  // lse[BR] then -delta[BR] (fp32)
   constexpr int kRowWaves = 2 * (BR / 64);      // waves that copy 64 of those floats per tile
   constexpr int kStage = (kRowOff + 8 * BR + 1023) / 1024 * 1024;  // one ring stage, 1 KB aligned
   constexpr int kPBlock = 2048;  // one 32 x 32 bf16 P block, 32 bytes per lane
@@ -520,7 +520,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
 #pragma unroll
         for (int s2 = 0; s2 < DS; ++s2) fr[s2] = RowFrag<E, QTile>::get(SR ? q_lds : do_lds, 32 * qb + l32, s2);
         __builtin_amdgcn_sched_barrier(0);
-        xs[qb] = f32x16_t{};
+        if constexpr (SR) {
+          xs[qb] = f32x16_t{};
+        } else {  // dP products start from -delta of each row, so they leave dP - delta
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4_t nd4 = *reinterpret_cast<const f32x4_t*>(dl_lds + 32 * qb + 8 * r4 + 4 * half);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xs[qb][4 * r4 + c] = nd4[c];
+          }
+        }
 #pragma unroll
         for (int s2 = 0; s2 < DS; ++s2) mma(xs[qb], fr[s2], kvf[s2]);
         hook(qb);
@@ -554,16 +563,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
           const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(ps + qb * kPBlock);
           const u32x4_t pb = *reinterpret_cast<const u32x4_t*>(ps + qb * kPBlock + 1024);
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int rb = 32 * qb + 8 * r4 + 4 * half;
-            const f32x4_t dl4 = *reinterpret_cast<const f32x4_t*>(dl_lds + rb);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int r = 4 * r4 + c;
-              const uint32_t word = (r < 8 ? pa : pb)[(r & 7) >> 1];
-              const float p = __uint_as_float((r & 1) ? (word & 0xFFFF0000u) : (word << 16));
-              xs[qb][r] = p * (xs[qb][r] - dl4[c]);
-            }
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t word = (r < 8 ? pa : pb)[(r & 7) >> 1];
+            const float p = __uint_as_float((r & 1) ? (word & 0xFFFF0000u) : (word << 16));
+            xs[qb][r] = p * xs[qb][r];  // xs already holds dP - delta
           }
         }
 #pragma unroll

@@ -40,7 +40,7 @@ struct Args {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;       // backward workspace: rowsum(dO * O), [B, Hq, Sq]
+  float* delta;       // backward workspace: -rowsum(dO * O) (stored negated), [B, Hq, Sq]
   float* lse2;        // backward workspace: lse * log2(e), [B, Hq, Sq]
   float* xpart;       // backward workspace: sink-split chunk partials, or null (no split)
   float* part;        // backward workspace: fp32 dK / dV partial sums of the head-group parts
@@ -173,7 +173,7 @@ inline size_t dkdv_chunk_bytes(const DkdvPlan& p, int B, int Hkv, int D) {
 inline size_t delta_bytes(int B, int Hq, int Sq) {
   return ((size_t)B * Hq * Sq * sizeof(float) + 255) / 256 * 256;
 }
-// Workspace layout: delta [B,Hq,Sq] f32 | lse * log2(e) [B,Hq,Sq] f32 | dK/dV partials (if the
+// Workspace layout: -delta [B,Hq,Sq] f32 | lse * log2(e) [B,Hq,Sq] f32 | dK/dV partials (if the
 // head group is split) | sink-split chunk partials (when the caller sized the workspace for them).
 inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   const DkdvPlan p = dkdv_plan(B, Hq, Hkv, Sk);
