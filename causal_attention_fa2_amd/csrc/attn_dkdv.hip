@@ -512,6 +512,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
       const int kw = kt * BC + 32 * pw;
       const int my_k = kw + l32;
       f32x16_t xs[QB];  // S -> P (S role) or dP -> dS (dP role)
+      Frag<E> pfr[QB][2];  // S role: P as the bf16 operand of dV += P^T dO
       // Phase 1: S = Q K^T and P (S role), dP = dO V^T (dP role).
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -552,8 +553,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
             }
           }
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-            *reinterpret_cast<u32x4_t*>(ps + qb * kPBlock + t * 1024) = acc_frag<E>(xs[qb], t).v;
+          for (int t = 0; t < 2; ++t) {
+            pfr[qb][t] = acc_frag<E>(xs[qb], t);  // the dV operand too: converted once
+            *reinterpret_cast<u32x4_t*>(ps + qb * kPBlock + t * 1024) = pfr[qb][t].v;
+          }
         }
       }
       // Phase 2: dV += P^T dO (S role); dS = P o (dP - delta), dK += dS^T Q (dP role).
@@ -574,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
           Frag<E> tr[DB];  // dO^T (S role) or Q^T (dP role), rows 32*qb + 16t ..
 #pragma unroll
           for (int db = 0; db < DB; ++db) tr[db] = TrFrag<E, QTile>::get(SR ? do_lds : q_lds, 32 * qb + 16 * t, 32 * db);
-          const Frag<E> af = acc_frag<E>(xs[qb], t);
+          const Frag<E> af = SR ? pfr[qb][t] : acc_frag<E>(xs[qb], t);
 #pragma unroll
           for (int db = 0; db < DB; ++db) mma(acc[db], af, tr[db]);
         }
