@@ -30,19 +30,20 @@ namespace fa {
 // paragraph: a per-sequence block table maps token positions to pool blocks); S is then the
 // sequence's own key count.
 // VL: packed documents (docs); a query sees only keys from its own document's start on.
-template <class E, int D, int NW, int KB, int NST, bool PG, bool VL>
+template <class E, int D, int NW, int KB, int NH, int NST, bool PG, bool VL>
 __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
     int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale_log2,
     int n_qt, PagedKV pg, Docs docs) {
   constexpr int BR = 32 * NW;
-  constexpr int BC = 32 * KB;
+  constexpr int BC = 32 * KB;  // keys per softmax update
+  constexpr int BT = BC * NH;  // keys per ring stage (NH updates per workgroup barrier)
   constexpr int DS = D / 16;  // 16-wide contraction steps over the head dimension
   constexpr int DB = D / 32;  // 32-wide output blocks over the head dimension
-  typedef LdsTile<E, BC, D> KvTile;
+  typedef LdsTile<E, BT, D> KvTile;
   constexpr int kStage = 2 * KvTile::kBytes;
-  constexpr int kOps = 2 * dma_tile_ops<E, BC, D, NW>();  // DMA instructions per wave per stage
+  constexpr int kOps = 2 * dma_tile_ops<E, BT, D, NW>();  // DMA instructions per wave per stage
   static_assert(NST == 2 || NST == 3, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[NST * kStage];
   __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
@@ -86,27 +87,27 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
 
   // key tiles: the sink tiles [0, jt_ns) then the window tiles [jt_lo, jt_hi]
   int jt_ns, jt_lo, jt_hi;
-  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BC, causal, window, sink, &jt_ns, &jt_lo,
+  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, BT, causal, window, sink, &jt_ns, &jt_lo,
                 &jt_hi);
-  if constexpr (VL) jt_lo = imax_(jt_lo, doc_start(cu_s, docs.n, q0 + off) / BC);  // no sinks here
+  if constexpr (VL) jt_lo = imax_(jt_lo, doc_start(cu_s, docs.n, q0 + off) / BT);  // no sinks here
   const int n_steps = jt_ns + jt_hi - jt_lo + 1;
   auto tile_of = [&](int s) __attribute__((always_inline)) { return s < jt_ns ? s : jt_lo + s - jt_ns; };
 
-  const uint32_t dma_off = dma_fast_ok<E, BC, D, NW>() ? dma_lane_off<KvTile, NW>() : 0;  // whole tiles
+  const uint32_t dma_off = dma_fast_ok<E, BT, D, NW>() ? dma_lane_off<KvTile, NW>() : 0;  // whole tiles
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
-    const int j0 = tile_of(s) * BC;
+    const int j0 = tile_of(s) * BT;
     if constexpr (PG) {
       const int* tab = pg.table + (size_t)b * pg.max_blocks;
-      dma_tile_paged<E, BC, D, NW>(stg, K, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
-      dma_tile_paged<E, BC, D, NW>(stg + KvTile::kBytes, V, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
-    } else if (dma_fast_ok<E, BC, D, NW>() && j0 + BC <= S) {
-      if constexpr (dma_fast_ok<E, BC, D, NW>()) {
-        dma_tile_fast<E, BC, D, NW>(stg, k_bg, j0, dma_off);
-        dma_tile_fast<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, dma_off);
+      dma_tile_paged<E, BT, D, NW>(stg, K, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
+      dma_tile_paged<E, BT, D, NW>(stg + KvTile::kBytes, V, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
+    } else if (dma_fast_ok<E, BT, D, NW>() && j0 + BT <= S) {
+      if constexpr (dma_fast_ok<E, BT, D, NW>()) {
+        dma_tile_fast<E, BT, D, NW>(stg, k_bg, j0, dma_off);
+        dma_tile_fast<E, BT, D, NW>(stg + KvTile::kBytes, v_bg, j0, dma_off);
       }
     } else {
-      dma_tile<E, BC, D, NW>(stg, k_bg, j0, S);
-      dma_tile<E, BC, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
+      dma_tile<E, BT, D, NW>(stg, k_bg, j0, S);
+      dma_tile<E, BT, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
     }
   };
   issue(0, ring);
@@ -123,7 +124,8 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   float m = kNegInf;  // running max of base-2 scores
   float l = 0.f;      // running sum of exp2(score - m) over this lane's keys
 
-  auto compute_general = [&](int j0, const char* k_lds, bool full) __attribute__((always_inline)) {
+  // one softmax update over the BC keys j0 .. j0 + BC - 1, stored from row kr0 of the stage
+  auto compute_general = [&](int j0, const char* k_lds, bool full, int kr0) __attribute__((always_inline)) {
     const char* v_lds = k_lds + KvTile::kBytes;
 
     // S^T = K Q^T for KB blocks of 32 keys: lane owns query my_q, registers hold keys. Each key
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     for (int kb = 0; kb < KB; ++kb) {
       Frag<E> kfr[DS];
 #pragma unroll
-      for (int s2 = 0; s2 < DS; ++s2) kfr[s2] = RowFrag<E, KvTile>::get(k_lds, 32 * kb + l32, s2);
+      for (int s2 = 0; s2 < DS; ++s2) kfr[s2] = RowFrag<E, KvTile>::get(k_lds, kr0 + 32 * kb + l32, s2);
       __builtin_amdgcn_sched_barrier(0);
       st[kb] = f32x16_t{};
 #pragma unroll
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     // The first key block's V^T fragments travel during the softmax.
     Frag<E> vt[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) vt[db] = TrFrag<E, KvTile>::get(v_lds, 0, 32 * db);
+    for (int db = 0; db < DB; ++db) vt[db] = TrFrag<E, KvTile>::get(v_lds, kr0, 32 * db);
     __builtin_amdgcn_sched_barrier(0);
 
     // Row max of the raw scores (scale > 0 commutes with max); masked keys become -inf, in place
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
       Frag<E> nv[DB];
       if (kt2 + 1 < 2 * KB) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) nv[db] = TrFrag<E, KvTile>::get(v_lds, 16 * (kt2 + 1), 32 * db);
+        for (int db = 0; db < DB; ++db) nv[db] = TrFrag<E, KvTile>::get(v_lds, kr0 + 16 * (kt2 + 1), 32 * db);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) mma(acc[db], vt[db], pf[kt2 / 2][kt2 % 2]);
@@ -210,15 +212,18 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   };
 
   auto compute = [&](int s, const char* k_lds) __attribute__((always_inline)) {
-    const int j0 = tile_of(s) * BC;
-    if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink)) return;
-    bool full = block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink);
-    if constexpr (VL) {
-      // every key before the first row's document start: empty; all after the last row's: full
-      if (j0 + BC - 1 < __builtin_amdgcn_readlane(ds_lane, 0)) return;
-      full = full && __builtin_amdgcn_readlane(ds_lane, 31) <= j0;
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+      const int j0 = tile_of(s) * BT + hb * BC;
+      if (block_empty(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink)) continue;
+      bool full = block_full(pw, pw + 31, j0, j0 + BC - 1, S, causal, window, sink);
+      if constexpr (VL) {
+        // every key before the first row's document start: empty; all after the last row's: full
+        if (j0 + BC - 1 < __builtin_amdgcn_readlane(ds_lane, 0)) continue;
+        full = full && __builtin_amdgcn_readlane(ds_lane, 31) <= j0;
+      }
+      compute_general(j0, k_lds, full, hb * BC);
     }
-    compute_general(j0, k_lds, full);
   };
 
   ring_run<NST, kStage, kOps>(ring, n_steps, issue, compute);
@@ -248,13 +253,13 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
 // S = 4096 and no different on the S_q = 1024 / 1 shapes), f32 three. Key tiles: 64 keys, 128 for
 // bf16 with D = 64 (half the products per key block, so a longer tile per step: 12% faster there);
 // the paged copy takes at most 64 rows per tile.
-template <class E, int D, int NW, bool PG, bool VL>
+template <class E, int D, int NW, bool PG, bool VL, int NH = 1>
 static void launch_fwd_nw(const Args& a) {
   constexpr int KB = E::kBytes == 2 ? (PG ? 2 : (D == 64 ? 4 : 2)) : 1;  // paged: tiles of at most 64 rows
   constexpr int NST = E::kBytes == 2 ? kFwdStages : 3;
   const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NST, PG, VL>), dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(NW * 64),
+  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NH, NST, PG, VL>), dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(NW * 64),
                      0, (hipStream_t)a.stream, (const typename E::T*)a.q, (const typename E::T*)a.k,
                      (const typename E::T*)a.v, (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
                      a.causal, a.window, a.sink, scale_log2, n_qt, a.pg, a.docs);
@@ -272,6 +277,7 @@ static int launch_fwd_t(const Args& a) {
     if (a.paged) launch_fwd_nw<E, D, kFwdWaves, true, false>(a);
     else if (a.docs.cu) launch_fwd_nw<E, D, kShortWaves, false, true>(a);
     else if (short_key_ranges(a)) launch_fwd_nw<E, D, kShortWaves, false, false>(a);
+    else if (mid_key_ranges(a)) launch_fwd_nw<E, D, kFwdWaves, false, false, 2>(a);
     else launch_fwd_nw<E, D, kFwdWaves, false, false>(a);
   } else {
     if (a.paged) launch_fwd_nw<E, D, 4, true, false>(a);

@@ -103,6 +103,22 @@ inline bool short_key_ranges(const Args& a) {
   if (a.window > 0 && mean > a.window) mean = a.window;
   return mean <= kShortKeys;
 }
+// Medium key ranges (same mean, more than kShortKeys and at most kMidKeys keys per row): the
+// 8-wave bf16 forward takes two softmax updates of 32*KB keys per workgroup barrier, from LDS stages
+// of twice the keys (the same bits as one update per barrier). Measured against one update per
+// barrier: 2% faster at dense causal S = 4096 (D = 128) and S = 8192 (D = 64), 5% with a 2048-key
+// window at S = 8192, no different at dense causal S = 8192 (D = 128), 1-1.5% slower at S = 16384
+// and S = 32768. dQ with the same stages was 1.5% slower at S = 4096 and keeps one block per barrier.
+#ifndef ATTN_MID_KEYS
+#define ATTN_MID_KEYS 4096
+#endif
+constexpr int kMidKeys = ATTN_MID_KEYS;
+inline bool mid_key_ranges(const Args& a) {
+  if (a.docs.cu) return false;
+  double mean = a.causal ? (a.Sk + 1) / 2.0 : (double)a.Sk;
+  if (a.window > 0 && mean > a.window) mean = a.window;
+  return mean <= kMidKeys;
+}
 
 // dK/dV decomposition: a workgroup of kDkdvWaves waves owns 32*kDkdvWaves keys and processes key
 // tile j and then key tile n_kt-1-j (equal work per workgroup under the causal mask). When that
