@@ -43,7 +43,12 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   constexpr int DB = D / 32;  // 32-wide output blocks over the head dimension
   typedef LdsTile<E, BT, D> KvTile;
   constexpr int kStage = 2 * KvTile::kBytes;
-  constexpr int kOps = 2 * dma_tile_ops<E, BT, D, NW>();  // DMA instructions per wave per stage
+  // Waves 0 .. CW-1 issue the tile copies: all of them, except in the 8-wave bf16 workgroup with two
+  // 64-key updates per stage at D = 128, where waves 0-3 (which the SIMDs serve first, so they wait
+  // at the barrier for waves 4-7) issue them all: 2-3% faster there, 1% slower with D = 64 or one
+  // update per stage.
+  constexpr int CW = E::kBytes == 2 && !PG && NW == 8 && NH == 2 && D == 128 ? 4 : NW;
+  constexpr int kOps = 2 * dma_tile_ops<E, BT, D, CW>();  // DMA instructions per copying wave per stage
   static_assert(NST == 2 || NST == 3, "ring depth");
   __shared__ __attribute__((aligned(1024))) char ring[NST * kStage];
   __shared__ int cu_s[VL ? kMaxDocs + 1 : 1];
@@ -93,21 +98,23 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   const int n_steps = jt_ns + jt_hi - jt_lo + 1;
   auto tile_of = [&](int s) __attribute__((always_inline)) { return s < jt_ns ? s : jt_lo + s - jt_ns; };
 
-  const uint32_t dma_off = dma_fast_ok<E, BT, D, NW>() ? dma_lane_off<KvTile, NW>() : 0;  // whole tiles
+  const bool copier = w < CW;
+  const uint32_t dma_off = dma_fast_ok<E, BT, D, CW>() && copier ? dma_lane_off<KvTile, CW>() : 0;  // whole tiles
   auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
     const int j0 = tile_of(s) * BT;
     if constexpr (PG) {
       const int* tab = pg.table + (size_t)b * pg.max_blocks;
       dma_tile_paged<E, BT, D, NW>(stg, K, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
       dma_tile_paged<E, BT, D, NW>(stg + KvTile::kBytes, V, tab, g, Hkv, pg.shift, pg.num_blocks, j0, S);
-    } else if (dma_fast_ok<E, BT, D, NW>() && j0 + BT <= S) {
-      if constexpr (dma_fast_ok<E, BT, D, NW>()) {
-        dma_tile_fast<E, BT, D, NW>(stg, k_bg, j0, dma_off);
-        dma_tile_fast<E, BT, D, NW>(stg + KvTile::kBytes, v_bg, j0, dma_off);
+    } else if (!copier) {
+    } else if (dma_fast_ok<E, BT, D, CW>() && j0 + BT <= S) {
+      if constexpr (dma_fast_ok<E, BT, D, CW>()) {
+        dma_tile_fast<E, BT, D, CW>(stg, k_bg, j0, dma_off);
+        dma_tile_fast<E, BT, D, CW>(stg + KvTile::kBytes, v_bg, j0, dma_off);
       }
     } else {
-      dma_tile<E, BT, D, NW>(stg, k_bg, j0, S);
-      dma_tile<E, BT, D, NW>(stg + KvTile::kBytes, v_bg, j0, S);
+      dma_tile<E, BT, D, CW>(stg, k_bg, j0, S);
+      dma_tile<E, BT, D, CW>(stg + KvTile::kBytes, v_bg, j0, S);
     }
   };
   issue(0, ring);
