@@ -34,8 +34,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
     const typename E::T* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ LSE2,
     float* __restrict__ delta, typename E::T* __restrict__ dQ,
     int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale,
-    float scale_log2, int n_qt, Docs docs) {
-  constexpr int BR = 32 * NW;
+    float scale_log2, int n_qt, int gp, Docs docs) {
   constexpr int BC = 32 * KB;
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
@@ -52,23 +51,26 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // Same order as the forward: heaviest query tiles first, a KV group's heads on one XCD.
+  // Same decomposition and order as the forward: gp query heads of one KV group per workgroup
+  // (wave w: head w % gp of the chunk, rows q0 + 32 * (w / gp) ..), heaviest query tiles first, a
+  // KV group's workgroups on one XCD.
+  const int BR = 32 * NW / gp;
   const int G = Hq / Hkv;
   const int BG = B * Hkv;
   const int bg = blockIdx.x % BG;
   const int rest = blockIdx.x / BG;
-  const int hh = rest % G;
-  const int rank = rest / G;
+  const int hc = rest % (G / gp);
+  const int rank = rest / (G / gp);
   const int qt = causal ? n_qt - 1 - rank : rank;
   const int b = bg / Hkv;
-  const int h = (bg - b * Hkv) * G + hh;
+  const int h = (bg - b * Hkv) * G + hc * gp + w % gp;
   const int off = S - Sq;  // query row r stands at key position r + off
   const size_t q_off = (size_t)(b * Hq + h) * Sq * D;
   const typename E::T* k_bg = K + (size_t)bg * S * D;
   const typename E::T* v_bg = V + (size_t)bg * S * D;
 
   const int q0 = qt * BR;
-  const int qw = q0 + 32 * w;
+  const int qw = q0 + 32 * (w / gp);
   const int my_q = qw + l32;
   const bool q_ok = my_q < Sq;
   const int pw = qw + off;  // positions of this wave's rows
@@ -224,11 +226,13 @@ static void launch_dq_nw(const Args& a) {
   typedef typename E::T T;
   constexpr int KB = E::kBytes == 2 ? (NW == 4 ? 2 : (D == 64 ? 4 : 2)) : 1;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-  const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
-  hipLaunchKernelGGL((dq_kernel<E, D, NW, KB, VL>), dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(NW * 64), 0,
+  const int gp = heads_per_workgroup(a.Hq / a.Hkv, NW, ATTN_DQ_HEAD_PACK);
+  const int br = 32 * NW / gp;  // query positions per workgroup
+  const int n_qt = (a.Sq + br - 1) / br;
+  hipLaunchKernelGGL((dq_kernel<E, D, NW, KB, VL>), dim3((unsigned)(n_qt * a.B * a.Hq / gp)), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                      (const T*)a.o_in, (const float*)a.lse, a.lse2, a.delta, (T*)a.dq, a.B, a.Hq, a.Hkv, a.Sq,
-                     a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt, a.docs);
+                     a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt, gp, a.docs);
 }
 
 // Waves per workgroup as in the forward: 8 (bf16; kShortWaves for short key ranges) or 4 (fp32).

@@ -35,8 +35,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
     int B, int Hq, int Hkv, int Sq, int S, int causal, int window, int sink, float scale_log2,
-    int n_qt, PagedKV pg, Docs docs) {
-  constexpr int BR = 32 * NW;
+    int n_qt, int gp, PagedKV pg, Docs docs) {
   constexpr int BC = 32 * KB;  // keys per softmax update
   constexpr int BT = BC * NH;  // keys per ring stage (NH updates per workgroup barrier)
   constexpr int DS = D / 16;  // 16-wide contraction steps over the head dimension
@@ -58,16 +57,20 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
+  // gp query heads of one KV group share a workgroup (and its K / V tiles): wave w takes head
+  // w % gp of the workgroup's head chunk and query rows q0 + 32 * (w / gp) .. + 31, so the
+  // workgroup covers BR = 32 * NW / gp query positions.
+  const int BR = 32 * NW / gp;
   const int G = Hq / Hkv;
   const int BG = B * Hkv;
   const int bg = blockIdx.x % BG;
   const int rest = blockIdx.x / BG;
-  const int hh = rest % G;
-  const int rank = rest / G;
+  const int hc = rest % (G / gp);
+  const int rank = rest / (G / gp);
   const int qt = causal ? n_qt - 1 - rank : rank;
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
-  const int h = g * G + hh;
+  const int h = g * G + hc * gp + w % gp;
 
   if constexpr (PG) S = imin_(imax_(pg.seqlen[b], Sq), pg.max_blocks << pg.shift);
   const int off = S - Sq;  // query row r stands at key position r + off
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 ? 2 : 1) void fwd_kernel(
   const typename E::T* v_bg = V + (size_t)bg * S * D;
 
   const int q0 = qt * BR;
-  const int qw = q0 + 32 * w;  // first row of this wave
+  const int qw = q0 + 32 * (w / gp);  // first row of this wave
   const int my_q = qw + l32;   // the query row this lane owns
   const bool q_ok = my_q < Sq;
   const int pw = qw + off;     // positions of this wave's rows: pw .. pw + 31
@@ -264,12 +267,14 @@ template <class E, int D, int NW, bool PG, bool VL, int NH = 1>
 static void launch_fwd_nw(const Args& a) {
   constexpr int KB = E::kBytes == 2 ? (PG ? 2 : (D == 64 ? 4 : 2)) : 1;  // paged: tiles of at most 64 rows
   constexpr int NST = E::kBytes == 2 ? kFwdStages : 3;
-  const int n_qt = (a.Sq + 32 * NW - 1) / (32 * NW);
+  const int gp = PG ? 1 : heads_per_workgroup(a.Hq / a.Hkv, NW, ATTN_FWD_HEAD_PACK);
+  const int br = 32 * NW / gp;  // query positions per workgroup
+  const int n_qt = (a.Sq + br - 1) / br;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NH, NST, PG, VL>), dim3((unsigned)(n_qt * a.B * a.Hq)), dim3(NW * 64),
-                     0, (hipStream_t)a.stream, (const typename E::T*)a.q, (const typename E::T*)a.k,
+  hipLaunchKernelGGL((fwd_kernel<E, D, NW, KB, NH, NST, PG, VL>), dim3((unsigned)(n_qt * a.B * a.Hq / gp)),
+                     dim3(NW * 64), 0, (hipStream_t)a.stream, (const typename E::T*)a.q, (const typename E::T*)a.k,
                      (const typename E::T*)a.v, (typename E::T*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
-                     a.causal, a.window, a.sink, scale_log2, n_qt, a.pg, a.docs);
+                     a.causal, a.window, a.sink, scale_log2, n_qt, gp, a.pg, a.docs);
 }
 
 // Ring depth: bf16 two stages (one tile in flight; measured about 1% faster than three at
