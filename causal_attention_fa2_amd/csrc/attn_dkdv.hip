@@ -408,9 +408,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     n_steps = hpg * nq;
   };
   // Query tiles run from the last one down, head by head; (hh, it) = head offset, tile counter.
-  // The S-role waves 0 .. CW-1 issue the Q / dO tile copies (waves 0 and 1 also the lse / delta
-  // rows), so the dP-role waves, whose steps take longer, never wait for copy instructions: 1.5-3.5%
-  // faster than copies shared by all eight waves at D = 128, no different at D = 64.
+  // The S-role waves 0 .. CW-1 issue the Q / dO tile copies right after each barrier (waves 0 and 1
+  // also the lse / delta rows), so the dP-role waves, whose steps take longer, never wait for copy
+  // instructions: 1.5-3.5% faster than copies shared by all eight waves at D = 128, no different at
+  // D = 64; with all eight waves copying, copies spread between the products of a step had been 1%
+  // faster, with the S-role waves copying they are 1-1.5% slower than copies right after the barrier.
   constexpr int CW = NP;
   constexpr bool kFast = dma_fast_ok<E, BR, D, CW>();
   const bool copier = w < CW;
@@ -431,31 +433,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     if (w < kRowWaves) {  // wave 2c copies lse rows 64c.., wave 2c+1 the delta rows 64c..
       const int c = w >> 1;
       dma_row_floats(stg + kRowOff + (w & 1) * 4 * BR + 256 * c, ((w & 1) ? delta : LSE2) + bh * Sq, i0 + 64 * c, Sq);
-    }
-  };
-  // At D = 128, whole-tile copies go out in two halves inside a step (the Q tile and the rows after
-  // the first block's products, the dO tile after the second's): issued right after the barrier,
-  // every wave of the compute unit waits there for its copy instructions (≈ 700 cycles per step,
-  // measured); spread between products the step is ≈ 1% shorter. At D = 64 (half the bytes) the
-  // spread step was 1-2% slower, so it copies right after the barrier.
-  constexpr bool kSpread = D == 128;
-  static_assert(!kSpread || QB == 2, "the two copy halves ride on the two row blocks of a step");
-  auto tile_whole = [&](int it) __attribute__((always_inline)) {
-    return kSpread && kFast && (lo + nq - 1 - it) * BR + BR <= Sq;
-  };
-  auto issue_half = [&](int hh, int it, char* stg, int part) __attribute__((always_inline)) {
-    if constexpr (kFast) {
-      const int i0 = (lo + nq - 1 - it) * BR;
-      const size_t bh = (size_t)b * Hq + h0 + hh;
-      if (part == 0) {
-        if (copier) dma_tile_fast<E, BR, D, CW>(stg, Q + bh * Sq * D, i0, dma_off);
-        if (w < kRowWaves) {
-          const int c = w >> 1;
-          dma_row_floats(stg + kRowOff + (w & 1) * 4 * BR + 256 * c, ((w & 1) ? delta : LSE2) + bh * Sq, i0 + 64 * c, Sq);
-        }
-      } else if (copier) {
-        dma_tile_fast<E, BR, D, CW>(stg + QTile::kBytes, dO + bh * Sq * D, i0, dma_off);
-      }
     }
   };
   auto advance = [&](int& hh, int& it) __attribute__((always_inline)) {
@@ -509,7 +486,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     // One 64-row query tile. Blocks of 32 rows that see none of this pair's keys
     // (the causal diagonal, window edges) are computed like partial ones: every P is 0, so they
     // add exact zeros to dV and dK.
-    auto compute = [&](int it, const char* q_lds, char* ps, auto&& hook) __attribute__((always_inline)) {
+    auto compute = [&](int it, const char* q_lds, char* ps) __attribute__((always_inline)) {
       const char* do_lds = q_lds + QTile::kBytes;
       const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
       const float* dl_lds = lse_lds + BR;
@@ -539,7 +516,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
         }
 #pragma unroll
         for (int s2 = 0; s2 < DS; ++s2) mma(xs[qb], fr[s2], kvf[s2]);
-        hook(qb);
         if constexpr (SR) {
           bool full = block_full(r0, r0 + 31, kw, kw + 31, S, causal, window, sink);
           if constexpr (VL) full = full && r0 + 31 < __builtin_amdgcn_readlane(de_lane, 0);
@@ -602,40 +578,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
         const int sp = sc == 0 ? 2 : sc - 1;  // stage of tile k - 1
         wait_vmcnt<0>();
         barrier_keep_vm();
-        if constexpr (kSpread) {
-          const bool next = k + 1 < n_steps;
-          const bool split = next && tile_whole(iq);  // tile k + 1 goes out in halves during the step
-          if (next && !split) issue(ih, iq, ring + sn * kStage);
-          auto hook = [&](int part) __attribute__((always_inline)) {
-            if (part < 2 && split) issue_half(ih, iq, ring + sn * kStage, part);
-          };
-          const bool mine = SR ? k < n_steps : k > 0;  // does this wave compute in this interval
-          if (!mine && split) {
-            hook(0);
-            hook(1);
-          }
-          if (mine) {
-            if constexpr (SR) compute(ct, ring + sc * kStage, pslot + (k & 1) * kPBuf, hook);
-            else compute(ct, ring + sp * kStage, pslot + ((k - 1) & 1) * kPBuf, hook);
+        if (k + 1 < n_steps) {
+          issue(ih, iq, ring + sn * kStage);
+          advance(ih, iq);
+        }
+        if constexpr (SR) {
+          if (k < n_steps) {
+            compute(ct, ring + sc * kStage, pslot + (k & 1) * kPBuf);
             advance(ch, ct);
           }
-          if (next) advance(ih, iq);
         } else {
-          auto no_hook = [](int) {};
-          if (k + 1 < n_steps) {
-            issue(ih, iq, ring + sn * kStage);
-            advance(ih, iq);
-          }
-          if constexpr (SR) {
-            if (k < n_steps) {
-              compute(ct, ring + sc * kStage, pslot + (k & 1) * kPBuf, no_hook);
-              advance(ch, ct);
-            }
-          } else {
-            if (k > 0) {
-              compute(ct, ring + sp * kStage, pslot + ((k - 1) & 1) * kPBuf, no_hook);
-              advance(ch, ct);
-            }
+          if (k > 0) {
+            compute(ct, ring + sp * kStage, pslot + ((k - 1) & 1) * kPBuf);
+            advance(ch, ct);
           }
         }
         sc = sn;
