@@ -226,7 +226,7 @@ static void launch_dq_nw(const Args& a) {
   typedef typename E::T T;
   constexpr int KB = E::kBytes == 2 ? (NW == 4 ? 2 : (D == 64 ? 4 : 2)) : 1;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-  const int gp = heads_per_workgroup(a.Hq / a.Hkv, NW, ATTN_DQ_HEAD_PACK);
+  const int gp = heads_per_workgroup(a.Hq / a.Hkv, NW, ATTN_DQ_HEAD_PACK, a.B, a.Hq, a.Sq);
   const int br = 32 * NW / gp;  // query positions per workgroup
   const int n_qt = (a.Sq + br - 1) / br;
   hipLaunchKernelGGL((dq_kernel<E, D, NW, KB, VL>), dim3((unsigned)(n_qt * a.B * a.Hq / gp)), dim3(NW * 64), 0,

@@ -267,7 +267,7 @@ template <class E, int D, int NW, bool PG, bool VL, int NH = 1>
 static void launch_fwd_nw(const Args& a) {
   constexpr int KB = E::kBytes == 2 ? (PG ? 2 : (D == 64 ? 4 : 2)) : 1;  // paged: tiles of at most 64 rows
   constexpr int NST = E::kBytes == 2 ? kFwdStages : 3;
-  const int gp = PG ? 1 : heads_per_workgroup(a.Hq / a.Hkv, NW, ATTN_FWD_HEAD_PACK);
+  const int gp = PG ? 1 : heads_per_workgroup(a.Hq / a.Hkv, NW, ATTN_FWD_HEAD_PACK, a.B, a.Hq, a.Sq);
   const int br = 32 * NW / gp;  // query positions per workgroup
   const int n_qt = (a.Sq + br - 1) / br;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);

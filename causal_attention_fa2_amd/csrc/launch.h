@@ -133,9 +133,14 @@ inline bool mid_key_ranges(const Args& a) {
 #ifndef ATTN_DQ_HEAD_PACK
 #define ATTN_DQ_HEAD_PACK 8
 #endif
-inline int heads_per_workgroup(int G, int NW, int cap) {
+// Fewer heads while that leaves fewer than kPackMinGroups workgroups (a handful of query rows, e.g.
+// one decode query per head: one head per workgroup spreads the heads over more compute units).
+constexpr int kPackMinGroups = 256;
+inline int heads_per_workgroup(int G, int NW, int cap, int B, int Hq, int Sq) {
   int gp = 1;
   while (gp * 2 <= cap && G % (gp * 2) == 0 && NW % (gp * 2) == 0) gp *= 2;
+  auto groups = [&](int p) { return (long long)((Sq + 32 * NW / p - 1) / (32 * NW / p)) * B * (Hq / p); };
+  while (gp > 1 && groups(gp) < kPackMinGroups) gp /= 2;
   return gp;
 }
 
