@@ -45,6 +45,13 @@ SMALL_CASES = [
     ("bf16", 1, 4, 2, 643, 64, True, 127),
     ("bf16", 2, 8, 2, 515, 64, True, 129),
     ("bf16", 1, 4, 1, 257, 64, True, 128),
+    # enough heads x rows for the forward / dQ workgroups to take several query heads of a KV group
+    # (at least 256 workgroups after packing): 4-wave and 8-wave workgroups, a ragged last tile, a
+    # window, and a group of 16 heads split into several packed chunks
+    ("f32", 8, 32, 4, 300, 64, True, 0),
+    ("bf16", 8, 32, 4, 300, 128, True, 0),
+    ("bf16", 2, 16, 2, 2200, 128, True, 0),
+    ("bf16", 4, 32, 2, 1000, 64, True, 300),
 ]
 
 
