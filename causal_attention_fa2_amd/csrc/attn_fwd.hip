@@ -6,19 +6,20 @@
 // "The custom CUDA kernel" (one window parameter for full-causal and sliding-window; the
 // log-sum-exp is saved for the backward); Grip paragraph of the first page for the head groups.
 //
-// Work decomposition (one workgroup = NW waves = 32*NW query rows of one (batch, query head)):
-//   * each wave owns 32 query rows; its Q rows stay in registers for the whole kernel as the
+// Work decomposition (one workgroup = NW waves of 32 query rows: gp query heads of one KV group x
+// 32*NW/gp query positions, gp = heads_per_workgroup):
+//   * each wave owns 32 query rows of one head; its Q rows stay in registers for the whole kernel as the
 //     B operand of S^T = K Q^T (one accumulator column per query, so every lane owns one query:
 //     the row max / row sum are in-lane plus one permlane32 swap with the partner lane);
-//   * key / value tiles of 32*KB rows stream through a ring of NST swizzled LDS tiles filled by
+//   * key / value tiles of 32*KB*NH rows stream through a ring of NST swizzled LDS tiles filled by
 //     LDS-DMA (global_load_lds_dwordx4): the next NST-1 tiles are in flight while tile s is used,
-//     with one workgroup barrier per tile;
+//     with one workgroup barrier per tile and NH softmax updates of 32*KB keys per tile;
 //   * P^T stays in registers and is the B operand of O^T = V^T P^T; V^T comes from LDS with the
 //     gfx950 transposing read, so V is never transposed in memory;
 //   * key tiles outside a wave's causal / window band are skipped, only boundary tiles are masked;
 //   * softmax runs in base 2 (scale * log2 e folded into one FMA per score); the O accumulator
 //     is rescaled only when a row max grows by more than 2^8; lse is exported as ln.
-//   * grid order: heaviest query tiles first; within one tile index the query heads of a KV group
+//   * grid order: heaviest query tiles first; within one tile index the head chunks of a KV group
 //     are consecutive multiples of B*Hkv apart, so with round-robin XCD dispatch a KV group's
 //     workgroups share one XCD (and its L2) when B*Hkv is a multiple of 8.
 #include "device.h"
