@@ -218,9 +218,9 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
   }
 }
 
-// Key tiles: bf16 with 8 waves 64 keys (128 for D = 64: 3% faster); bf16 with 4 waves 64 keys (two
-// workgroups share a compute unit; at D = 128 4% faster than 32 keys on packed documents, at D = 64
-// 128 keys were 4-10% slower on the window workloads); fp32 32 keys.
+// Key tiles: bf16 with 4 waves 64 keys (two workgroups share a compute unit; at D = 128 4% faster
+// than 32 keys on packed documents, at D = 64 128 keys were 4-10% slower on the window workloads);
+// bf16 with 8 waves (no longer launched) 64 keys, 128 for D = 64; fp32 32 keys.
 template <class E, int D, int NW, bool VL>
 static void launch_dq_nw(const Args& a) {
   typedef typename E::T T;
@@ -235,14 +235,15 @@ static void launch_dq_nw(const Args& a) {
                      a.Sk, a.causal, a.window, a.sink, a.scale, scale_log2, n_qt, gp, a.docs);
 }
 
-// Waves per workgroup as in the forward: 8 (bf16; kShortWaves for short key ranges) or 4 (fp32).
+// Waves per workgroup: 4, two workgroups per compute unit, for every shape. Against 8-wave
+// workgroups (one per compute unit) on the dense and long-window shapes: 1% faster at S = 4096 and
+// 8192, 3% on ragged 2777 x 3001, within 1% either way at S = 32768 and with a 2048-key window.
 template <class E, int D>
 static int launch_bwd_t(const Args& a) {
   notify_launch("attn_bwd_dq", 0, a.stream);
   if constexpr (E::kBytes == 2) {
     if (a.docs.cu) launch_dq_nw<E, D, kShortWaves, true>(a);
-    else if (short_key_ranges(a)) launch_dq_nw<E, D, kShortWaves, false>(a);
-    else launch_dq_nw<E, D, 8, false>(a);
+    else launch_dq_nw<E, D, kShortWaves, false>(a);
   } else {
     if (a.docs.cu) launch_dq_nw<E, D, 4, true>(a);
     else launch_dq_nw<E, D, 4, false>(a);

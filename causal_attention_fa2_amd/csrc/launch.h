@@ -80,11 +80,12 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int max_keys, int 
 #define ATTN_FWD_STAGES 2
 #endif
 constexpr int kFwdWaves = ATTN_FWD_WAVES, kFwdStages = ATTN_FWD_STAGES;
-// Waves per workgroup of the bf16 forward and dQ passes when the visible key range of a row is short:
-// a workgroup walks the union of its waves' key ranges, which for 32*NW rows exceeds one wave's by
-// up to 32*(NW-1) keys. Measured against 8 waves: forward 6-15% and dQ 9-15% faster on the
-// sliding-window (W = 1024) and packed-document (1.1-1.7k-token) workloads and on dense causal
-// S = 1024; dense causal S = 4096 (2k keys per row on average) is 1.5% slower.
+// Waves per workgroup of the bf16 forward pass when the visible key range of a row is short (and of
+// the bf16 dQ pass always): a workgroup walks the union of its waves' key ranges, which for 32*NW rows
+// exceeds one wave's by up to 32*(NW-1) keys. Measured against 8 waves: forward 6-15% and dQ 9-15%
+// faster on the sliding-window (W = 1024) and packed-document (1.1-1.7k-token) workloads and on dense
+// causal S = 1024; at dense causal S = 4096 the forward is 1.5% slower and dQ (with packed heads) 1%
+// faster.
 #ifndef ATTN_SHORT_WAVES
 #define ATTN_SHORT_WAVES 4
 #endif
