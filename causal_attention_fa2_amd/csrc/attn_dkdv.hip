@@ -306,7 +306,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
   typedef LdsTile<E, BR, D> QTile;
-  constexpr int kTileOps = dma_tile_ops<E, BR, D, NW>();
   static_assert(BR == dkdv_query_rows(D) && BC == 32 * kDkdvWaves, "the host plan assumes these tiles");
   static_assert(BR % 64 == 0 && 2 * (BR / 64) <= NW, "one row copy (64 floats) per wave");
   constexpr int kRowOff = 2 * QTile::kBytes;  // lse[BR] then -delta[BR] (fp32)
