@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Forward + backward causal GQA attention throughput on one MI355X.
 
-One step = attn_fwd then attn_bwd (dQ kernel with the delta rows, dK/dV kernel) over one batch
-of synthetic input already resident in HBM. Default workload: B=1, Hq=64, Hkv=8, S=4096, D=128,
+One step = attn_fwd then attn_bwd over one batch of synthetic input already resident in HBM; the
+backward gets a workspace sized by attn_bwd_qk_workspace_bytes_for, so at the default workload it
+runs the delta rows, the dK/dV kernel (which also stores dS), its head-split reduce and the dQ
+kernel that reads the stored dS. Default workload: B=1, Hq=64, Hkv=8, S=4096, D=128,
 bf16, causal. Prints one JSON line.
 
 FLOPs are counted as 4*B*Hq*N*D for the forward, with N = S^2/2 attended pairs under the causal
@@ -35,6 +37,7 @@ KERNEL_SOURCES = {  # the files a kernel's code and launch configuration come fr
     "attn_fwd": ["attn_fwd.hip", "device.h", "tiles.h", "launch.h"],
     "attn_bwd_dkdv": ["attn_dkdv.hip", "device.h", "tiles.h", "launch.h"],
     "attn_bwd_dq": ["attn_bwd.hip", "device.h", "tiles.h", "launch.h"],
+    "attn_bwd_prep": ["attn_bwd.hip", "device.h", "launch.h"],
     "attn_bwd_dkdv_reduce": ["attn_dkdv.hip", "device.h", "launch.h"],
     "attn_bwd_dkdv_chunks": ["attn_dkdv.hip", "device.h", "launch.h"],
 }

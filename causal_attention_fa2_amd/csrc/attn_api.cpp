@@ -131,11 +131,19 @@ int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const vo
   a.delta = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + row_bytes);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_bytes);
-  // a workspace sized by attn_bwd_qk_workspace_bytes_for holds the sink-split slots after the rest
+  // a workspace sized by attn_bwd_qk_workspace_bytes_for holds, after the rest, the sink-split
+  // slots or the stored dS (a mask has at most one of the two; the stored dS is used in bf16)
   const size_t base_bytes = fa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D);
   const size_t full_bytes = fa::bwd_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, causal, window, sink);
-  if (full_bytes > base_bytes && workspace_bytes >= full_bytes)
-    a.xpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + base_bytes);
+  if (full_bytes > base_bytes && workspace_bytes >= full_bytes) {
+    char* extra = static_cast<char*>(workspace) + base_bytes;
+    if (fa::ds_bytes(B, Hq, Hkv, Sq, Sk, causal, window, sink) == 0) {
+      a.xpart = reinterpret_cast<float*>(extra);
+    } else if (dtype == fa::kBF16) {
+      a.dsm = fa::ds_map(Hq, Hkv, Sq, Sk, causal);
+      a.dsm.ds = reinterpret_cast<uint16_t*>(extra);
+    }
+  }
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

@@ -21,11 +21,41 @@
 //      few workgroups to fill the GPU, the head group is split into `hs` parts whose fp32 partial
 //      sums go to the workspace and
 //   3. dkdv_reduce_kernel (attn_dkdv.hip) adds them in a fixed order (deterministic) and rounds to the element type.
+// With a stored dS (bf16, a mask without a window or sinks, a workspace with room for it; layout
+// at DsMap in launch.h) the order is bwd_prep_kernel (the delta and base-2 log-sum-exp rows), the
+// dK / dV pass, which also writes each dS block it forms, its reduce, and dq_ds_kernel, which
+// reads those blocks for dQ = scale * dS K: no score or dP products in the dQ pass.
 // P and dS are rounded to the element type only as MFMA operands; all sums are fp32.
 #include "device.h"
 #include "launch.h"
 
 namespace fa {
+
+// This lane's half of sum_d dO_id * O_id for query row `o_row` (lanes l and l ^ 32 hold the two
+// halves of the row: elements 16s + 8h .. +7, h = l / 32), from the dO fragments `df` of the same
+// elements; pair_sum of it is delta_i. dq_kernel and bwd_prep_kernel both form delta through it.
+template <class E, int D>
+__device__ __forceinline__ float half_row_dot(const typename E::T* __restrict__ o_row, const Frag<E>* df,
+                                              bool ok) {
+  constexpr int DS = D / 16;
+  const int half = lane_id() >> 5;
+  float dl = 0.f;
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    const Frag<E> of = load_frag_global(o_row + 16 * s + 8 * half, ok);
+    if constexpr (E::kBytes == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dl += bf16_to_f32(of.v[e] & 0xFFFFu) * bf16_to_f32(df[s].v[e] & 0xFFFFu);
+        dl += bf16_to_f32(of.v[e] >> 16) * bf16_to_f32(df[s].v[e] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dl += of.lo[e] * df[s].lo[e] + of.hi[e] * df[s].hi[e];
+    }
+  }
+  return dl;
+}
 
 template <class E, int D, int NW, int KB, bool VL>
 __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq_kernel(
@@ -116,22 +146,7 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
   }
   const size_t row_idx = (size_t)(b * Hq + h) * Sq + (q_ok ? my_q : 0);
   // delta_i = sum_d dO_id O_id: this lane holds half of row my_q's elements, its partner the rest
-  float dl = 0.f;
-#pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    const Frag<E> of = load_frag_global(O + q_off + (size_t)my_q * D + 16 * s + 8 * half, q_ok);
-    if constexpr (E::kBytes == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dl += bf16_to_f32(of.v[e] & 0xFFFFu) * bf16_to_f32(df[s].v[e] & 0xFFFFu);
-        dl += bf16_to_f32(of.v[e] >> 16) * bf16_to_f32(df[s].v[e] >> 16);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dl += of.lo[e] * df[s].lo[e] + of.hi[e] * df[s].hi[e];
-    }
-  }
-  dl = pair_sum(dl);
+  const float dl = pair_sum(half_row_dot<E, D>(O + q_off + (size_t)my_q * D, df, q_ok));
   const float l2 = LSE[row_idx] * kLog2e;  // base-2 log-sum-exp used by both gradient kernels
   const float nlse2 = -l2;
   if (q_ok && half == 0) {
@@ -218,6 +233,184 @@ __global__ __launch_bounds__(NW * 64, E::kBytes == 2 && NW == 4 ? 2 : 1) void dq
   }
 }
 
+// With a stored dS the rows' delta and base-2 log-sum-exp come first, from their own pass: one
+// wave per 32 rows of the flattened [B * Hq * Sq] rows, the same arithmetic as dq_kernel's.
+template <class E, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __restrict__ O,
+                                                       const typename E::T* __restrict__ dO,
+                                                       const float* __restrict__ LSE, float* __restrict__ LSE2,
+                                                       float* __restrict__ delta, long long rows) {
+  constexpr int DS = D / 16;
+  const int lane = lane_id();
+  const int half = lane >> 5;
+  const long long r = ((long long)blockIdx.x * 4 + wave_id()) * 32 + (lane & 31);
+  const bool ok = r < rows;
+  const size_t ro = (size_t)(ok ? r : 0);
+  Frag<E> df[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) df[s] = load_frag_global(dO + ro * D + 16 * s + 8 * half, ok);
+  const float dl = pair_sum(half_row_dot<E, D>(O + ro * D, df, ok));
+  if (ok && half == 0) {
+    delta[ro] = -dl;
+    LSE2[ro] = LSE[ro] * kLog2e;
+  }
+}
+
+// dQ from the stored dS (bf16; layout at DsMap): dQ^T += K^T dS^T over the key blocks of the
+// wave's rows, with no S or dP products. Wave w owns 64 query rows (two 32-row blocks) of head
+// w % gp of its KV group's chunk; per 32-key step the workgroup copies the K tile and each wave
+// its own two dS blocks (2 KB each, as the dK/dV pass wrote them) into a three-stage LDS ring.
+// Both operands come through transposing LDS reads: K^T as in dq_kernel, and dS^T (a lane per
+// query, 8 keys) from the block, whose chunk holds one key's values for 8 queries: within each
+// group of 16 lanes, lane s reads the four queries 16g + 4(s % 4) .. of key 4(s / 4) + .., i.e.
+// chunk g*64 + (s & 1)*32 + (key ^ 4*(2g + (s & 1))), bytes 8 * ((s >> 1) & 1) .. Every block of a
+// strip holds the exact dS of its pairs (zeros where the mask hides them), so no mask here.
+template <int D>
+__global__ __launch_bounds__(256, 2) void dq_ds_kernel(const uint16_t* __restrict__ K, uint16_t* __restrict__ dQ,
+                                                        DsMap dsm, int B, int Hq, int Hkv, int Sq, int S,
+                                                        int causal, float scale, int n_qt, int gp) {
+  typedef BF16 E;
+  constexpr int NW = 4;   // waves
+  constexpr int RB = 2;   // 32-row query blocks per wave
+  constexpr int DB = D / 32;
+  typedef LdsTile<E, 32, D> KTile;
+  constexpr int kStage = KTile::kBytes + NW * RB * 2048;
+  constexpr int kOps = dma_tile_ops<E, 32, D, NW>() + 2 * RB;
+  static_assert(dma_fast_ok<E, 32, D, NW>(), "whole K tiles copy with scalar bases");
+  __shared__ __attribute__((aligned(1024))) char ring[3 * kStage];
+
+  const int lane = lane_id();
+  const int w = wave_id();
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  // Decomposition and order as dq_kernel: gp heads of one KV group per workgroup, heaviest query
+  // tiles first, a KV group's workgroups on one XCD.
+  const int BR = 32 * RB * NW / gp;
+  const int G = Hq / Hkv;
+  const int BG = B * Hkv;
+  const int bg = blockIdx.x % BG;
+  const int rest = blockIdx.x / BG;
+  const int hc = rest % (G / gp);
+  const int rank = rest / (G / gp);
+  const int qt = causal ? n_qt - 1 - rank : rank;
+  const int b = bg / Hkv;
+  const int h = (bg - b * Hkv) * G + hc * gp + w % gp;
+  const int off = S - Sq;
+  const uint16_t* k_bg = K + (size_t)bg * S * D;
+  const int q0 = qt * BR;
+  const int qw = q0 + 32 * RB * (w / gp);
+  const int ib = qw / 32;  // this wave's first query block
+  const int hg = hc * gp + w % gp;  // head within the KV group
+  const char* ds_base = reinterpret_cast<const char*>(dsm.ds);
+
+  // key blocks of the workgroup's rows (no window, no sinks)
+  int jt_ns, jt_lo, jt_hi;
+  kv_tile_range(q0 + off, imin_(q0 + BR - 1, Sq - 1) + off, S, 32, causal, 0, 0, &jt_ns, &jt_lo, &jt_hi);
+  const int n_steps = jt_hi - jt_lo + 1;
+  // block (query block i, key block j) lies in the strip of i: written by the dK/dV pass
+  auto in_strip = [&](int i, int j) __attribute__((always_inline)) {
+    return i < dsm.nqb && j < ds_strip_len(dsm, i);
+  };
+  const uint32_t k_off = dma_lane_off<KTile, NW>();
+  auto issue = [&](int s, char* stg) __attribute__((always_inline)) {
+    const int j = jt_lo + s;
+    if ((j + 1) * 32 <= S) dma_tile_fast<E, 32, D, NW>(stg, k_bg, 32 * j, k_off);
+    else dma_tile<E, 32, D, NW>(stg, k_bg, 32 * j, S);
+    const uint32_t dl = lds_addr(stg + KTile::kBytes + w * RB * 2048);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      // blocks outside the strip are not read back; their copy takes the region's first block
+      const int i = ib + rb;
+      const char* src = ds_base + (in_strip(i, j) ? ds_block_off(dsm, bg, hg, i, j) : 0);
+      dma16_s(lane * 16, src, dl + rb * 2048);
+      dma16_s(lane * 16, src + 1024, dl + rb * 2048 + 1024);
+    }
+  };
+  issue(0, ring);
+  if (n_steps > 1) issue(1, ring + kStage);
+
+  f32x16_t acc[RB][DB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[rb][db] = f32x16_t{};
+  // transposing-read addresses of this lane inside a dS block, for keys 16t + 4h + (s >> 2) (+ 8)
+  const int s16 = lane & 15;
+  const int g = (lane >> 4) & 1;
+  const int hw = s16 & 1;
+  auto ds_off = [&](int key) __attribute__((always_inline)) {
+    return ((g * 64 + hw * 32 + (key ^ (4 * (2 * g + hw)))) << 4) + 8 * ((s16 >> 1) & 1);
+  };
+  auto compute = [&](int s, const char* stg) __attribute__((always_inline)) {
+    const int j = jt_lo + s;
+    const char* ds_lds = stg + KTile::kBytes + w * RB * 2048;
+    bool act[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) act[rb] = in_strip(ib + rb, j);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      Frag<E> kt[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) kt[db] = TrFrag<E, KTile>::get(stg, 16 * t, 32 * db);
+      const int ka = 16 * t + 4 * half + (s16 >> 2);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if (!act[rb]) continue;
+        const char* blk = ds_lds + rb * 2048;
+        s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)((__attribute__((address_space(3))) char*)(blk + ds_off(ka))));
+        s16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)((__attribute__((address_space(3))) char*)(blk + ds_off(ka + 8))));
+        Frag<E> f;
+        const u32x2_t ux = __builtin_bit_cast(u32x2_t, x);
+        const u32x2_t uy = __builtin_bit_cast(u32x2_t, y);
+        f.v = u32x4_t{ux[0], ux[1], uy[0], uy[1]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) mma(acc[rb][db], kt[db], f);
+      }
+    }
+  };
+  ring_run<3, kStage, kOps>(ring, n_steps, issue, compute);
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int my_q = qw + 32 * rb + l32;
+    if (my_q >= Sq) continue;
+    uint16_t* dq_row = dQ + ((size_t)(b * Hq + h) * Sq + my_q) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + 8 * r4 + 4 * half;
+        const float x0 = acc[rb][db][4 * r4 + 0] * scale, x1 = acc[rb][db][4 * r4 + 1] * scale;
+        const float x2 = acc[rb][db][4 * r4 + 2] * scale, x3 = acc[rb][db][4 * r4 + 3] * scale;
+        *reinterpret_cast<u32x2_t*>(dq_row + d) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+      }
+    }
+  }
+}
+
+template <int D>
+static void launch_dq_ds(const Args& a) {
+  constexpr int NW = 4, RB = 2;
+  const int G = a.Hq / a.Hkv;
+  // heads per workgroup: up to 4 (one per wave, all at the same 64 rows), fewer while that
+  // leaves under kPackMinGroups workgroups
+  int gp = 1;
+  while (gp * 2 <= NW && G % (gp * 2) == 0) gp *= 2;
+  auto groups = [&](int p) {
+    const int br = 32 * RB * NW / p;
+    return (long long)((a.Sq + br - 1) / br) * a.B * (a.Hq / p);
+  };
+  while (gp > 1 && groups(gp) < kPackMinGroups) gp /= 2;
+  const int br = 32 * RB * NW / gp;
+  const int n_qt = (a.Sq + br - 1) / br;
+  hipLaunchKernelGGL((dq_ds_kernel<D>), dim3((unsigned)(n_qt * a.B * a.Hq / gp)), dim3(NW * 64), 0,
+                     (hipStream_t)a.stream, (const uint16_t*)a.k, (uint16_t*)a.dq, a.dsm, a.B, a.Hq, a.Hkv,
+                     a.Sq, a.Sk, a.causal, a.scale, n_qt, gp);
+}
+
 // Key tiles: bf16 with 4 waves 64 keys (two workgroups share a compute unit; at D = 128 4% faster
 // than 32 keys on packed documents, at D = 64 128 keys were 4-10% slower on the window workloads);
 // bf16 with 8 waves (no longer launched) 64 keys, 128 for D = 64; fp32 32 keys.
@@ -240,6 +433,22 @@ static void launch_dq_nw(const Args& a) {
 // 8192, 3% on ragged 2777 x 3001, within 1% either way at S = 32768 and with a 2048-key window.
 template <class E, int D>
 static int launch_bwd_t(const Args& a) {
+  if constexpr (E::kBytes == 2) {
+    if (a.dsm.ds != nullptr) {  // delta rows, dK / dV with the stored dS, then dQ from it
+      typedef typename E::T T;
+      const long long rows = (long long)a.B * a.Hq * a.Sq;
+      notify_launch("attn_bwd_prep", 0, a.stream);
+      hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((rows + 127) / 128)), dim3(256), 0,
+                         (hipStream_t)a.stream, (const T*)a.o_in, (const T*)a.dout, (const float*)a.lse,
+                         a.lse2, a.delta, rows);
+      notify_launch("attn_bwd_prep", 1, a.stream);
+      if (launch_dkdv(a) != 0) return -1;
+      notify_launch("attn_bwd_dq", 0, a.stream);
+      launch_dq_ds<D>(a);
+      notify_launch("attn_bwd_dq", 1, a.stream);
+      return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+  }
   notify_launch("attn_bwd_dq", 0, a.stream);
   if constexpr (E::kBytes == 2) {
     if (a.docs.cu) launch_dq_nw<E, D, kShortWaves, true>(a);

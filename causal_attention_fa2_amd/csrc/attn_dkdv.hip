@@ -297,7 +297,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ part, int B, int Hq,
     int Hkv, int Sq, int S, int causal, int window, int sink, float scale, float scale_log2,
-    int n_kt, int n_pairs, int hs, Docs docs, float* __restrict__ xpart, int nc, int c_lo, int c_len) {
+    int n_kt, int n_pairs, int hs, Docs docs, float* __restrict__ xpart, int nc, int c_lo, int c_len,
+    DsMap dsm) {
   typedef BF16 E;
   constexpr int NW = 8;        // waves
   constexpr int NP = 4;        // wave pairs, 32 keys each
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
     // One 64-row query tile. Blocks of 32 rows that see none of this pair's keys
     // (the causal diagonal, window edges) are computed like partial ones: every P is 0, so they
     // add exact zeros to dV and dK.
-    auto compute = [&](int it, const char* q_lds, char* ps) __attribute__((always_inline)) {
+    auto compute = [&](int hh, int it, const char* q_lds, char* ps) __attribute__((always_inline)) {
       const char* do_lds = q_lds + QTile::kBytes;
       const float* lse_lds = reinterpret_cast<const float*>(q_lds + kRowOff);
       const float* dl_lds = lse_lds + BR;
@@ -540,9 +541,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
           }
         }
       }
-      // Phase 2: dV += P^T dO (S role); dS = P o (dP - delta), dK += dS^T Q (dP role).
+      // Phase 2: dV += P^T dO (S role); dS = P o (dP - delta), dK += dS^T Q (dP role), and with
+      // a stored dS its blocks that lie in their query block's strip (the rest are all zero: no
+      // visible pair) go out as they enter the products.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
+        char* ds_dst = nullptr;
+        if constexpr (!SR) {
+          const int i = i0 / 32 + qb, kb = kt * (BC / 32) + pw;
+          if (dsm.ds != nullptr && i < dsm.nqb && kb < ds_strip_len(dsm, i))
+            ds_dst = reinterpret_cast<char*>(dsm.ds) + ds_block_off(dsm, bg, hp * hpg + hh, i, kb);
+        }
         if constexpr (!SR) {
           const u32x4_t pa = *reinterpret_cast<const u32x4_t*>(ps + qb * kPBlock);
           const u32x4_t pb = *reinterpret_cast<const u32x4_t*>(ps + qb * kPBlock + 1024);
@@ -559,6 +568,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
 #pragma unroll
           for (int db = 0; db < DB; ++db) tr[db] = TrFrag<E, QTile>::get(SR ? do_lds : q_lds, 32 * qb + 16 * t, 32 * db);
           const Frag<E> af = SR ? pfr[qb][t] : acc_frag<E>(xs[qb], t);
+          // chunk t*64 + half*32 + (key ^ 4*(2t + half)) of the block; streamed past the caches
+          // (read back by the dQ pass only after this pass: 12% faster dQ than cached stores)
+          if (!SR && ds_dst != nullptr)
+            __builtin_nontemporal_store(
+                af.v, reinterpret_cast<u32x4_t*>(ds_dst + t * 1024 + half * 512 + ((l32 ^ (8 * t + 4 * half)) << 4)));
 #pragma unroll
           for (int db = 0; db < DB; ++db) mma(acc[db], af, tr[db]);
         }
@@ -575,7 +589,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
       for (int k = 0; k <= n_steps; ++k) {
         const int sn = sc == 2 ? 0 : sc + 1;  // stage of tile k + 1
         const int sp = sc == 0 ? 2 : sc - 1;  // stage of tile k - 1
-        wait_vmcnt<0>();
+        // only the S-role waves copy; the dP-role waves' own memory operations are the stored dS
+        // blocks, which nothing here waits for
+        if constexpr (SR) wait_vmcnt<0>();
         barrier_keep_vm();
         if (k + 1 < n_steps) {
           issue(ih, iq, ring + sn * kStage);
@@ -583,12 +599,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_pair_kernel(
         }
         if constexpr (SR) {
           if (k < n_steps) {
-            compute(ct, ring + sc * kStage, pslot + (k & 1) * kPBuf);
+            compute(ch, ct, ring + sc * kStage, pslot + (k & 1) * kPBuf);
             advance(ch, ct);
           }
         } else {
           if (k > 0) {
-            compute(ct, ring + sp * kStage, pslot + ((k - 1) & 1) * kPBuf);
+            compute(ch, ct, ring + sp * kStage, pslot + ((k - 1) & 1) * kPBuf);
             advance(ch, ct);
           }
         }
@@ -700,7 +716,7 @@ static int launch_dkdv_t(const Args& a) {
                          (const T*)a.dout, (const float*)a.lse2, (const float*)a.delta, (T*)a.dk,
                          (T*)a.dv, a.part, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.window, a.sink,
                          a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs, a.docs, a.xpart, p.nc, p.c_lo,
-                         p.c_len);
+                         p.c_len, a.dsm);
     } else {
       auto kern = a.docs.cu ? dkdv_kernel<E, D, NW, QB, true> : dkdv_kernel<E, D, NW, QB, false>;
       hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, st, (const T*)a.q, (const T*)a.k,

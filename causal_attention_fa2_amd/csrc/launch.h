@@ -3,6 +3,7 @@
 #define ATTN_LAUNCH_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #include "tiles.h"
 
@@ -28,6 +29,63 @@ struct Docs {
 };
 constexpr int kMaxDocs = 2047;
 
+// Stored dS of the bf16 backward. The dK/dV pass forms every 32 x 32 block of
+// dS = P o (dP - delta) of its visited tiles in registers (rounded to bf16, the operand of
+// dK += dS^T Q); when the caller's workspace has room it also writes them out, and the dQ pass
+// reads them back for dQ = dS K instead of recomputing S = Q K^T and dP = dO V^T (a third of its
+// matrix products; the pages' backward recomputes the score tiles, which is what the pass does
+// without the room). Masks without a window or sink keys only.
+// Which blocks: query block i (rows 32i .. 32i+31) needs key blocks 0 .. n(i)-1, n(i) =
+// min(nkb, i + c) (c = nkb without the causal mask: every key). Layout, per (batch, KV head):
+// one entry per 64-row query tile t and key block j < min(nkb, 2t + 1 + c) (the keys of the tile's
+// second block), entries in order of t then j; an entry holds the G query heads of the group in
+// order, each as its two 32-row blocks (2 KB each). A dQ workgroup of several heads at the same
+// rows so reads one contiguous run per key block (runs of 2 KB per head and block were 22%
+// slower to stream). A block is 2 KB: sixteen-byte chunk t*64 + h*32 + (k ^ 4*(2t + h)) holds key
+// k's dS for queries 16t + 4h + {0, 1, 2, 3, 8, 9, 10, 11} (t, h in {0, 1}) -- the way a lane of
+// the dK/dV pass holds them, so one block is written by two 1 KB stores per wave, with the key
+// index swizzled so that the dQ pass's transposing LDS reads hit distinct banks.
+struct DsMap {
+  uint16_t* ds;         // null: the dQ pass recomputes
+  int nqb, nkb;         // query / key blocks of 32
+  int c;                // see above
+  int G;                // query heads per KV head
+  long long per_group;  // entries per (batch, KV head)
+};
+ATTN_HD int ds_strip_len(const DsMap& m, int i) { return imin_(m.nkb, i + m.c); }
+// First entry of 64-row tile t: the tiles before it with fewer than nkb key blocks hold
+// c + 1, c + 3, ..
+ATTN_HD long long ds_tile_start(const DsMap& m, int t) {
+  const int x = m.nkb - m.c - 1;
+  const long long t1 = x <= 0 ? 0 : imin_((x + 1) / 2, t);
+  return t1 * (t1 - 1) + (long long)(m.c + 1) * t1 + (long long)(t - t1) * m.nkb;
+}
+// Byte offset of block (query block i, key block j) of head hg of KV head bg (= b * Hkv + g).
+ATTN_HD size_t ds_block_off(const DsMap& m, int bg, int hg, int i, int j) {
+  return (((size_t)bg * m.per_group + ds_tile_start(m, i >> 1) + j) * m.G + hg) * 4096 + (size_t)(i & 1) * 2048;
+}
+inline DsMap ds_map(int Hq, int Hkv, int Sq, int Sk, int causal) {
+  DsMap m;
+  m.ds = nullptr;
+  m.nqb = (Sq + 31) / 32;
+  m.nkb = (Sk + 31) / 32;
+  // causal: row 32i + 31 stands at position 32i + 31 + Sk - Sq and sees key blocks up to
+  // i + (31 + Sk - Sq) / 32
+  m.c = causal ? 1 + (31 + Sk - Sq) / 32 : m.nkb;
+  m.G = Hq / Hkv;
+  m.per_group = ds_tile_start(m, (m.nqb + 1) / 2);
+  return m;
+}
+// Bytes of the stored dS (0: not used for these arguments). At most kDsMaxBytes (a 4096-token
+// causal 64-head problem needs 1.1 GB; longer ones recompute).
+constexpr size_t kDsMaxBytes = (size_t)4 << 30;
+inline size_t ds_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int causal, int window, int sink) {
+  if (window != 0 || sink != 0) return 0;
+  const DsMap m = ds_map(Hq, Hkv, Sq, Sk, causal);
+  const size_t n = (size_t)B * Hq * (size_t)m.per_group * 4096;
+  return n <= kDsMaxBytes ? n : 0;
+}
+
 struct Args {
   int dtype;
   const void* q;
@@ -51,6 +109,7 @@ struct Args {
   bool paged;  // forward only: k, v are pools read through pg (Sk is then per sequence)
   PagedKV pg;
   Docs docs;   // packed documents (Sq = Sk, causal, no sinks)
+  DsMap dsm;   // backward: stored dS (dsm.ds null: none)
 };
 
 // The argument checks every entry point shares: ATTN_OK (0) or the attn_status_t of the first
@@ -215,7 +274,8 @@ inline size_t delta_bytes(int B, int Hq, int Sq) {
   return ((size_t)B * Hq * Sq * sizeof(float) + 255) / 256 * 256;
 }
 // Workspace layout: -delta [B,Hq,Sq] f32 | lse * log2(e) [B,Hq,Sq] f32 | dK/dV partials (if the
-// head group is split) | sink-split chunk partials (when the caller sized the workspace for them).
+// head group is split) | sink-split chunk partials or the stored dS (when the caller sized the
+// workspace for them; a mask has at most one of the two).
 inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D) {
   const DkdvPlan p = dkdv_plan(B, Hq, Hkv, Sk);
   size_t partials = p.hs > 1 ? (size_t)p.hs * 2 * B * Hkv * Sk * D * sizeof(float) : 0;
@@ -225,7 +285,8 @@ inline size_t bwd_workspace_bytes_for(int B, int Hq, int Hkv, int Sq, int Sk, in
                                       int window, int sink) {
   DkdvPlan p = dkdv_plan(B, Hq, Hkv, Sk);
   dkdv_sink_split(p, B, Hq, Hkv, Sq, Sk, D, window, sink, causal != 0);
-  return bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) + dkdv_chunk_bytes(p, B, Hkv, D);
+  return bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) + dkdv_chunk_bytes(p, B, Hkv, D) +
+         ds_bytes(B, Hq, Hkv, Sq, Sk, causal, window, sink);
 }
 
 }  // namespace fa

@@ -90,7 +90,9 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
 /* Backward. o and lse must be exactly what attn_fwd wrote for the same q, k, v and arguments.
  * dout [B,Hq,S,D] is the gradient of the loss with respect to o. Writes dq [B,Hq,S,D] and dk, dv
  * [B,Hkv,S,D]; all three are fully overwritten (not accumulated into). `workspace` is a device
- * buffer of at least attn_bwd_workspace_bytes(...) bytes; its contents on entry do not matter. */
+ * buffer of at least attn_bwd_workspace_bytes(...) bytes; its contents on entry do not matter.
+ * One of attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, S, S, D, causal, window, 0) bytes also holds
+ * the stored dS of a mask without a window (see there). */
 int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes,
@@ -108,14 +110,23 @@ int attn_fwd_qk(int dtype, const void* q, const void* k, const void* v, void* o,
  * and, when the head group is split, 2 * parts * B*Hkv*Sk*D fp32. 0 for rejected sizes. */
 size_t attn_bwd_qk_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D);
 
-/* Workspace bytes of attn_bwd_qk for these exact mask arguments: at least
- * attn_bwd_qk_workspace_bytes(...), plus, with a window and 1 <= sink <= 128 sink keys, room for
- * the sink split of the bf16 dK/dV pass. Every query past the window still sees the sink keys, so
- * the first 128-key tile has many times the work of any other; the split shares its query range
- * among several workgroups whose fp32 partial sums (2 * chunks * parts * B*Hkv*128*D) a small
- * reduce adds in a fixed order. attn_bwd_qk uses the split only when workspace_bytes is at least
- * this size (otherwise it runs unsplit, same results up to summation order). 0 for rejected
- * sizes. */
+/* Workspace bytes of attn_bwd_qk for these exact mask arguments: attn_bwd_qk_workspace_bytes(...)
+ * plus one of two optional regions that attn_bwd_qk uses only when workspace_bytes is at least
+ * this size (otherwise it runs without, same results up to summation order and rounding):
+ *  - with a window and 1 <= sink <= 128 sink keys, the sink split of the bf16 dK/dV pass. Every
+ *    query past the window still sees the sink keys, so the first 128-key tile has many times the
+ *    work of any other; the split shares its query range among several workgroups whose fp32
+ *    partial sums (2 * chunks * parts * B*Hkv*128*D) a small reduce adds in a fixed order.
+ *  - with neither a window nor sink keys, the stored dS (bf16 only; fp32 calls leave it unused):
+ *    the dK/dV pass writes every 32 x 32 block of dS = P o (dP - delta) it forms, rounded to bf16
+ *    as it enters dK, and the dQ pass computes dQ = scale * dS K from them instead of recomputing
+ *    the score and dP tiles ("KYNETRA FOUNDRY" page, FlashAttention paragraph, has the backward
+ *    recompute them: here that is the pass without this region). B*Hq * (sum over 32-row query
+ *    blocks i of the key blocks up to the one holding position 32i + 31 + Sk - Sq, all of them
+ *    without the causal mask) * 2048 bytes -- 1.08 GB for B=1, Hq=64, S=4096 -- and none above
+ *    4 GiB. dQ then differs from the recomputing pass by the bf16 rounding of P before dS is
+ *    formed (dK and dV are the same bits either way).
+ * 0 for rejected sizes. */
 size_t attn_bwd_qk_workspace_bytes_for(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
                                        int window, int sink);
 
@@ -133,8 +144,8 @@ int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const vo
  * comes from a static device array of ATTN_NOALLOC_SCRATCH_BYTES (one per device, held until the
  * process ends; enough for B=1, Hq=64, Hkv=8, S=4096, D=128 with its head split). Results are
  * bitwise those of attn_bwd_qk given a workspace of that size. Returns ATTN_ERR_SCRATCH, before
- * enqueueing anything, when attn_bwd_qk_workspace_bytes(...) exceeds the array; the sink split is
- * used only when attn_bwd_qk_workspace_bytes_for(...) fits. Allocates nothing. Every call on one
+ * enqueueing anything, when attn_bwd_qk_workspace_bytes(...) exceeds the array; the sink split or
+ * stored dS is used only when attn_bwd_qk_workspace_bytes_for(...) fits. Allocates nothing. Every call on one
  * device uses that device's array (the device of `stream`, or the current device for NULL), so
  * calls that overlap in time on one device race; nothing needs clearing between calls. */
 #define ATTN_NOALLOC_SCRATCH_BYTES (72u << 20)

@@ -91,7 +91,10 @@ def test_varlen_one_document_is_bitwise_plain():
     a = run_varlen(q, k, v, do, np.array([[0, S]], dtype=np.int32), dtype, 0)
     tq, tk, tv, tdo = upload(q, dtype), upload(k, dtype), upload(v, dtype), upload(do, dtype)
     o, lse = fa.forward(tq, tk, tv, True, 0)
-    dq, dk, dv = fa.backward(tq, tk, tv, o, lse, tdo, True, 0)
+    # the plain workspace: dQ recomputes the score tiles, as the packed-document pass always does
+    # (a workspace with room for the stored dS changes dQ's rounding, not dK / dV)
+    ws = torch.empty(fa.attn_bwd_workspace_bytes(1, Hq, Hkv, S, D), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = fa.backward(tq, tk, tv, o, lse, tdo, True, 0, workspace=ws)
     torch.cuda.synchronize()
     for name, t in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
         b = t.double().cpu().numpy()

@@ -23,15 +23,22 @@ def _problem(dtype, B, Hq, Hkv, Sq, Sk, D, window, sink, seed):
     return q, k, v, o, lse, do
 
 
+def _workspace_bytes(B, Hq, Hkv, Sq, Sk, D, window, sink):
+    """The workspace the static array stands for: sized by attn_bwd_qk_workspace_bytes_for (sink
+    split or stored dS on) when that fits in the array, else the plain size."""
+    import causal_attention_fa2_amd as fa
+    need = fa.attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, True, window, sink)
+    return need if need <= fa.ATTN_NOALLOC_SCRATCH_BYTES else fa.attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
+
+
 def _with_workspace(p, window, sink):
-    """attn_bwd_qk given a workspace sized by attn_bwd_qk_workspace_bytes_for (every split on)."""
+    """attn_bwd_qk given an allocated workspace of _workspace_bytes(...)."""
     import torch
     import causal_attention_fa2_amd as fa
     q, k, v, o, lse, do = p
     B, Hq, Sq, D = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
-    ws = torch.empty(fa.attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, True, window, sink),
-                     dtype=torch.uint8, device=q.device)
+    ws = torch.empty(_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, window, sink), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fa.attn_bwd_qk(q, k, v, o, lse, do, dq, dk, dv, ws, True, window, None, None, sink)
     return dq, dk, dv
@@ -46,13 +53,16 @@ def _noalloc(p, window, sink):
     return dq, dk, dv
 
 
-# Calls in this order, each smaller than the one before (bytes of workspace it needs):
-#   the 64/8-head S=4096 D=128 bf16 backward with its head split (66 MiB of the 72 MiB array),
+# Calls in this order, each smaller than the one before (bytes of workspace it uses):
+#   the 64/8-head S=4096 D=128 bf16 backward with its head split (66 MiB of the 72 MiB array; its
+#   stored dS would not fit, so dQ recomputes),
 #   a sliding-window problem with 4 sink keys (sink split of key tile 0, chunk partials),
+#   a small bf16 causal problem with its stored dS,
 #   a small fp32 problem with fewer queries than keys.
 CALLS = [
     ("bf16", 1, 64, 8, 4096, 4096, 128, 0, 0),
     ("bf16", 1, 8, 2, 2048, 2048, 64, 128, 4),
+    ("bf16", 1, 8, 2, 700, 700, 128, 0, 0),
     ("f32", 1, 4, 2, 300, 700, 64, 0, 0),
 ]
 
@@ -60,9 +70,11 @@ CALLS = [
 def test_noalloc_matches_workspace_call_in_sequence():
     import torch
     import causal_attention_fa2_amd as fa
-    need = [fa.attn_bwd_qk_workspace_bytes_for(*c[1:7], True, c[7], c[8]) for c in CALLS]
-    assert need[0] > need[1] > need[2] > 0 and need[0] <= fa.ATTN_NOALLOC_SCRATCH_BYTES
+    need = [_workspace_bytes(*c[1:9]) for c in CALLS]
+    assert need[0] > need[1] > need[2] > need[3] > 0 and need[0] <= fa.ATTN_NOALLOC_SCRATCH_BYTES
+    assert need[0] == fa.attn_bwd_qk_workspace_bytes(*CALLS[0][1:7])  # no room for its stored dS
     assert need[1] > fa.attn_bwd_qk_workspace_bytes(*CALLS[1][1:7])  # the sink split is in use
+    assert need[2] > fa.attn_bwd_qk_workspace_bytes(*CALLS[2][1:7])  # the stored dS is in use
     for n, (dtype, B, Hq, Hkv, Sq, Sk, D, window, sink) in enumerate(CALLS):
         say(f"noalloc call {n}: {dtype} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} Sk={Sk} D={D} W={window} sink={sink}")
         p = _problem(dtype, B, Hq, Hkv, Sq, Sk, D, window, sink, 900 + 10 * n)
