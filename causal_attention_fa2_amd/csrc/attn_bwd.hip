@@ -23,8 +23,9 @@
 //   3. dkdv_reduce_kernel (attn_dkdv.hip) adds them in a fixed order (deterministic) and rounds to the element type.
 // With a stored dS (bf16, a mask without a window or sinks, a workspace with room for it; layout
 // at DsMap in launch.h) the order is bwd_prep_kernel (the delta and base-2 log-sum-exp rows), the
-// dK / dV pass, which also writes each dS block it forms, its reduce, and dq_ds_kernel, which
-// reads those blocks for dQ = scale * dS K: no score or dP products in the dQ pass.
+// dK / dV pass, which also writes each dS block it forms, and dq_ds_kernel, which reads those
+// blocks for dQ = scale * dS K (no score or dP products in the dQ pass) and, in trailing
+// workgroups, adds the dK / dV head-part partials.
 // P and dS are rounded to the element type only as MFMA operands; all sums are fp32.
 #include "device.h"
 #include "launch.h"
@@ -265,10 +266,55 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __re
 // group of 16 lanes, lane s reads the four queries 16g + 4(s % 4) .. of key 4(s / 4) + .., i.e.
 // chunk g*64 + (s & 1)*32 + (key ^ 4*(2g + (s & 1))), bytes 8 * ((s >> 1) & 1) .. Every block of a
 // strip holds the exact dS of its pairs (zeros where the mask hides them), so no mask here.
+// Workgroups n_dq.. of the same launch add the dK / dV head-part partials of a split head group
+// (what dkdv_reduce_kernel does otherwise, the same sums in the same order): the short reduce
+// fills in behind the dQ workgroups instead of taking a launch of its own (a prefill chunk's
+// backward 2% faster, S = 4096 0.5%).
+struct PartSum {
+  const float* part;  // 2 * hs slices of n floats: dK part 0, dV part 0, dK part 1, ..
+  uint16_t* dK;
+  uint16_t* dV;
+  size_t n;           // B * Hkv * S * D
+  int hs;             // 1: nothing to add
+  int n_dq;           // dQ workgroups before the reduce ones
+};
+constexpr int kPartChunks = 16;  // 1024-element chunks per reduce workgroup, loaded before any sum
 template <int D>
 __global__ __launch_bounds__(256, 2) void dq_ds_kernel(const uint16_t* __restrict__ K, uint16_t* __restrict__ dQ,
                                                         DsMap dsm, int B, int Hq, int Hkv, int Sq, int S,
-                                                        int causal, float scale, int n_qt, int gp) {
+                                                        int causal, float scale, int n_qt, int gp, PartSum ps) {
+  if ((int)blockIdx.x >= ps.n_dq) {
+    const size_t base = (size_t)(blockIdx.x - ps.n_dq) * kPartChunks * 1024 + threadIdx.x * 4;
+    f32x4_t sk[kPartChunks], sv[kPartChunks];
+#pragma unroll
+    for (int c = 0; c < kPartChunks; ++c) {
+      const size_t i = base + (size_t)c * 1024;
+      if (i < ps.n) {
+        sk[c] = *reinterpret_cast<const f32x4_t*>(ps.part + i);
+        sv[c] = *reinterpret_cast<const f32x4_t*>(ps.part + ps.n + i);
+      }
+    }
+    for (int p = 1; p < ps.hs; ++p) {
+#pragma unroll
+      for (int c = 0; c < kPartChunks; ++c) {
+        const size_t i = base + (size_t)c * 1024;
+        if (i < ps.n) {
+          sk[c] += *reinterpret_cast<const f32x4_t*>(ps.part + (size_t)(2 * p) * ps.n + i);
+          sv[c] += *reinterpret_cast<const f32x4_t*>(ps.part + (size_t)(2 * p + 1) * ps.n + i);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kPartChunks; ++c) {
+      const size_t i = base + (size_t)c * 1024;
+      if (i < ps.n) {
+        const f32x4_t k4 = sk[c] * scale, v4 = sv[c];
+        *reinterpret_cast<u32x2_t*>(ps.dK + i) = u32x2_t{pack_bf16x2(k4[0], k4[1]), pack_bf16x2(k4[2], k4[3])};
+        *reinterpret_cast<u32x2_t*>(ps.dV + i) = u32x2_t{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+      }
+    }
+    return;
+  }
   typedef BF16 E;
   constexpr int NW = 4;   // waves
   constexpr int RB = 2;   // 32-row query blocks per wave
@@ -406,9 +452,13 @@ static void launch_dq_ds(const Args& a) {
   while (gp > 1 && groups(gp) < kPackMinGroups) gp /= 2;
   const int br = 32 * RB * NW / gp;
   const int n_qt = (a.Sq + br - 1) / br;
-  hipLaunchKernelGGL((dq_ds_kernel<D>), dim3((unsigned)(n_qt * a.B * a.Hq / gp)), dim3(NW * 64), 0,
+  // the dK / dV head-part partials of a split head group are added by trailing workgroups
+  PartSum ps{a.part, (uint16_t*)a.dk, (uint16_t*)a.dv, (size_t)a.B * a.Hkv * a.Sk * D, 1, n_qt * a.B * a.Hq / gp};
+  ps.hs = dkdv_plan(a.B, a.Hq, a.Hkv, a.Sk).hs;
+  const int n_red = ps.hs > 1 ? (int)((ps.n + kPartChunks * 1024 - 1) / (kPartChunks * 1024)) : 0;
+  hipLaunchKernelGGL((dq_ds_kernel<D>), dim3((unsigned)(ps.n_dq + n_red)), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.k, (uint16_t*)a.dq, a.dsm, a.B, a.Hq, a.Hkv,
-                     a.Sq, a.Sk, a.causal, a.scale, n_qt, gp);
+                     a.Sq, a.Sk, a.causal, a.scale, n_qt, gp, ps);
 }
 
 // Key tiles: bf16 with 4 waves 64 keys (two workgroups share a compute unit; at D = 128 4% faster

@@ -725,7 +725,7 @@ static int launch_dkdv_t(const Args& a) {
                          a.sink, a.scale, scale_log2, p.n_kt, p.n_pairs, p.hs, a.docs);
     }
     notify_launch("attn_bwd_dkdv", 1, a.stream);
-    if (p.hs > 1) {
+    if (p.hs > 1 && a.dsm.ds == nullptr) {  // with a stored dS the dQ launch adds the parts
       const size_t n = (size_t)a.B * a.Hkv * a.Sk * D;
       dim3 rgrid((unsigned)((n / 4 + 255) / 256)), rblock(256);
       notify_launch("attn_bwd_dkdv_reduce", 0, a.stream);

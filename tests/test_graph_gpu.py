@@ -3,9 +3,9 @@ capture them in a HIP graph (torch.cuda.CUDAGraph). Each capture below is replay
 with the outputs overwritten by eager work between replays, and every replay must reproduce the
 eager call bit for bit (the kernels sum in a fixed order, so reruns are bitwise equal).
 
-Covered: forward + backward with the head-split reduce, the backward with the sink split and its
-chunk reduce, and the key-split decode forward with its combine. A last test runs two problems at
-once on two streams."""
+Covered: forward + backward with the head-split reduce, the same with the stored dS, the backward
+with the sink split and its chunk reduce, and the key-split decode forward with its combine. A
+last test runs two problems at once on two streams."""
 import math
 
 import numpy as np
@@ -78,6 +78,34 @@ def test_graph_forward_backward_head_split():
     want = [t.clone() for t in (o, lse, dq, dk, dv)]
     g = _capture(step)
     _replay_and_check(g, [o, lse, dq, dk, dv], want, "fwd+bwd")
+
+
+def test_graph_forward_backward_stored_ds():
+    """The same problem with a workspace sized by attn_bwd_qk_workspace_bytes_for: the backward runs
+    the delta rows, the dK/dV pass storing dS, and the dQ pass reading it (whose trailing
+    workgroups add the head-split partials)."""
+    import torch
+    import causal_attention_fa2_amd as fa
+    fa.attn_set_launch_hook(None)
+    B, Hq, Hkv, S, D = 1, 8, 2, 1000, 128
+    say("graph: forward + backward (stored dS, head split)")
+    q, k, v, do = _inputs("bf16", B, Hq, Hkv, S, S, D, 305)
+    scale = 1.0 / math.sqrt(D)
+    need = fa.attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, S, S, D, True, 0, 0)
+    assert need > fa.attn_bwd_workspace_bytes(B, Hq, Hkv, S, D)  # room for the stored dS
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o, lse = torch.empty_like(q), torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step():
+        fa.attn_fwd(q, k, v, o, lse, True, 0, scale)
+        fa.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, True, 0, scale)
+
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (o, lse, dq, dk, dv)]
+    g = _capture(step)
+    _replay_and_check(g, [o, lse, dq, dk, dv], want, "fwd+bwd stored dS")
 
 
 def test_graph_backward_sink_split():
