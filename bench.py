@@ -3,8 +3,8 @@
 
 One step = attn_fwd then attn_bwd over one batch of synthetic input already resident in HBM; the
 backward gets a workspace sized by attn_bwd_qk_workspace_bytes_for, so at the default workload it
-runs the delta rows, the dK/dV kernel (which also stores dS), its head-split reduce and the dQ
-kernel that reads the stored dS. Default workload: B=1, Hq=64, Hkv=8, S=4096, D=128,
+runs the delta rows, the dK/dV kernel (which also stores dS) and the dQ kernel that reads the stored
+dS (its trailing workgroups add the dK/dV head-split partials). Default workload: B=1, Hq=64, Hkv=8, S=4096, D=128,
 bf16, causal. Prints one JSON line.
 
 FLOPs are counted as 4*B*Hq*N*D for the forward, with N = S^2/2 attended pairs under the causal
@@ -411,7 +411,9 @@ def main() -> int:
     eb = 2 if w.dtype == "bf16" else 4
     nkv = w.B * w.Hkv * w.S * w.D
     parts = (ws_bytes - 2 * ((w.B * w.Hq * Sq * 4 + 255) // 256 * 256)) // (2 * nkv * 4)
-    hbm_bytes = {"attn_bwd_dkdv_reduce": 2 * nkv * (4 * max(parts, 1) + eb)}
+    hbm_bytes = {"attn_bwd_dkdv_reduce": 2 * nkv * (4 * max(parts, 1) + eb),
+                 # O and dO in, LSE in, -delta and lse * log2(e) out
+                 "attn_bwd_prep": 2 * w.B * w.Hq * Sq * w.D * eb + 12 * w.B * w.Hq * Sq}
 
     kernels = {}
     for name, t in kern_ms.items():
