@@ -201,10 +201,11 @@ int attn_decode_fwd(int dtype, const void* q, const void* k, const void* v, cons
 
 /* Optional launch observer, for profiling. When set, every entry point calls
  * hook(kernel, 0, stream, user) just before and hook(kernel, 1, stream, user) just after it
- * enqueues each of its kernels ("attn_fwd", "attn_bwd_dq" (which also forms the delta rows),
- * "attn_bwd_dkdv", "attn_bwd_dkdv_reduce" (only when the head group is split),
- * "attn_bwd_dkdv_chunks" (only when the sink key tile is split), "attn_decode",
- * "attn_decode_combine"),
+ * enqueues each of its kernels ("attn_fwd", "attn_bwd_prep" (the delta rows; only with a stored
+ * dS), "attn_bwd_dq" (which otherwise forms the delta rows, and with a stored dS also adds the
+ * head-part partials of a split head group), "attn_bwd_dkdv", "attn_bwd_dkdv_reduce" (only when
+ * the head group is split and dS is not stored), "attn_bwd_dkdv_chunks" (only when the sink key
+ * tile is split), "attn_decode", "attn_decode_combine"),
  * on the calling thread, so the hook can record timing events on `stream` around exactly one
  * kernel. NULL (the default) turns it off. The setting is process-wide; set it while no other
  * thread is calling the library. */
