@@ -137,7 +137,7 @@ int attn_bwd_qk(int dtype, const void* q, const void* k, const void* v, const vo
   const size_t full_bytes = fa::bwd_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, causal, window, sink);
   if (full_bytes > base_bytes && workspace_bytes >= full_bytes) {
     char* extra = static_cast<char*>(workspace) + base_bytes;
-    if (fa::ds_bytes(B, Hq, Hkv, Sq, Sk, causal, window, sink) == 0) {
+    if (fa::ds_bytes(B, Hq, Hkv, Sq, Sk, D, causal, window, sink) == 0) {
       a.xpart = reinterpret_cast<float*>(extra);
     } else if (dtype == fa::kBF16) {
       a.dsm = fa::ds_map(Hq, Hkv, Sq, Sk, causal);

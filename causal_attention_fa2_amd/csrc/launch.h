@@ -34,7 +34,7 @@ constexpr int kMaxDocs = 2047;
 // dK += dS^T Q); when the caller's workspace has room it also writes them out, and the dQ pass
 // reads them back for dQ = dS K instead of recomputing S = Q K^T and dP = dO V^T (a third of its
 // matrix products; the pages' backward recomputes the score tiles, which is what the pass does
-// without the room). Masks without a window or sink keys only.
+// without the room). Masks without a window or sink keys only; which shapes: ds_bytes.
 // Which blocks: query block i (rows 32i .. 32i+31) needs key blocks 0 .. n(i)-1, n(i) =
 // min(nkb, i + c) (c = nkb without the causal mask: every key). Layout, per (batch, KV head):
 // one entry per 64-row query tile t and key block j < min(nkb, 2t + 1 + c) (the keys of the tile's
@@ -77,10 +77,16 @@ inline DsMap ds_map(int Hq, int Hkv, int Sq, int Sk, int causal) {
   return m;
 }
 // Bytes of the stored dS (0: not used for these arguments). At most kDsMaxBytes (a 4096-token
-// causal 64-head problem needs 1.1 GB; longer ones recompute).
+// causal 64-head problem needs 1.1 GB; longer ones recompute). Only where it was measured to pay:
+// D = 128 and at least kDsMinKeys keys. A stored block saves two 32 x 32 x D products of the dQ
+// pass for 4 KB of HBM traffic and a pass of its own for the delta rows; against recomputing,
+// whole fwd + bwd steps (64/8 heads unless noted) took 1-2% less at S = 4096, 22-31% less for 1
+// or 100 queries against 4096 keys, the same at S = 2048, 12% more at S = 1024, and at D = 64
+// 17% more at S = 8192 (16 heads) and 2% more at S = 1024 (4 x 16 heads).
 constexpr size_t kDsMaxBytes = (size_t)4 << 30;
-inline size_t ds_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int causal, int window, int sink) {
-  if (window != 0 || sink != 0) return 0;
+constexpr int kDsMinKeys = 2048;
+inline size_t ds_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, int window, int sink) {
+  if (window != 0 || sink != 0 || D != 128 || Sk < kDsMinKeys) return 0;
   const DsMap m = ds_map(Hq, Hkv, Sq, Sk, causal);
   const size_t n = (size_t)B * Hq * (size_t)m.per_group * 4096;
   return n <= kDsMaxBytes ? n : 0;
@@ -286,7 +292,7 @@ inline size_t bwd_workspace_bytes_for(int B, int Hq, int Hkv, int Sq, int Sk, in
   DkdvPlan p = dkdv_plan(B, Hq, Hkv, Sk);
   dkdv_sink_split(p, B, Hq, Hkv, Sq, Sk, D, window, sink, causal != 0);
   return bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, D) + dkdv_chunk_bytes(p, B, Hkv, D) +
-         ds_bytes(B, Hq, Hkv, Sq, Sk, causal, window, sink);
+         ds_bytes(B, Hq, Hkv, Sq, Sk, D, causal, window, sink);
 }
 
 }  // namespace fa

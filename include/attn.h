@@ -92,7 +92,7 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
  * [B,Hkv,S,D]; all three are fully overwritten (not accumulated into). `workspace` is a device
  * buffer of at least attn_bwd_workspace_bytes(...) bytes; its contents on entry do not matter.
  * One of attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, S, S, D, causal, window, 0) bytes also holds
- * the stored dS of a mask without a window (see there). */
+ * the stored dS where that is used (see there). */
 int attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout, void* dq, void* dk, void* dv,
              void* workspace, size_t workspace_bytes,
@@ -117,7 +117,8 @@ size_t attn_bwd_qk_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D
  *    query past the window still sees the sink keys, so the first 128-key tile has many times the
  *    work of any other; the split shares its query range among several workgroups whose fp32
  *    partial sums (2 * chunks * parts * B*Hkv*128*D) a small reduce adds in a fixed order.
- *  - with neither a window nor sink keys, the stored dS (bf16 only; fp32 calls leave it unused):
+ *  - with neither a window nor sink keys, D = 128 and Sk >= 2048, the stored dS (bf16 only; fp32
+ *    calls leave it unused; where it was measured to pay):
  *    the dK/dV pass writes every 32 x 32 block of dS = P o (dP - delta) it forms, rounded to bf16
  *    as it enters dK, and the dQ pass computes dQ = scale * dS K from them instead of recomputing
  *    the score and dP tiles ("KYNETRA FOUNDRY" page, FlashAttention paragraph, has the backward

@@ -154,12 +154,12 @@ def test_qk_workspace_bytes_for(lib):
     assert fa.attn_bwd_qk_workspace_bytes_for(1, 2, 2, 64, 64, 64, True, 8, -1) == 0
 
 
-def _stored_ds_bytes(B, Hq, Sq, Sk, causal, window, sink):
+def _stored_ds_bytes(B, Hq, Sq, Sk, D, causal, window, sink):
     """Room for the stored dS: per (batch, query head) and 64-row query tile, two 2 KB blocks (its two
     32-row halves) per 32-key block from key 0 up to the one holding the position the tile's last
     nominal row stands at (row 64t + 63 at position 64t + 63 + Sk - Sq), all key blocks without the
-    causal mask; none with a window or sink keys, or beyond 4 GiB."""
-    if window or sink:
+    causal mask; none with a window or sink keys, for D = 64, below 2048 keys, or beyond 4 GiB."""
+    if window or sink or D != 128 or Sk < 2048:
         return 0
     nkb = -(-Sk // 32)
     entries = 0
@@ -174,21 +174,27 @@ def test_qk_workspace_bytes_for_stored_ds(lib):
     """Without a window and sink keys attn_bwd_qk_workspace_bytes_for adds the stored dS after the
     plain workspace (attn_bwd_qk_workspace_bytes stays the plain size)."""
     for B, Hq, Hkv, Sq, Sk, D, causal in ((1, 64, 8, 4096, 4096, 128, True), (1, 64, 8, 4096, 4096, 128, False),
-                                          (2, 4, 2, 300, 700, 64, True), (1, 8, 2, 1000, 1000, 128, True),
-                                          (1, 4, 4, 7, 7, 64, True), (1, 4, 2, 33, 100, 64, True),
-                                          (3, 6, 2, 130, 130, 64, False), (1, 64, 8, 8192, 8192, 128, True),
-                                          (1, 64, 8, 32768, 32768, 128, True), (1, 64, 8, 1, 4096, 128, True)):
+                                          (2, 4, 2, 300, 2100, 128, True), (1, 8, 2, 2049, 2049, 128, True),
+                                          (1, 4, 4, 7, 2048, 128, True), (1, 4, 2, 33, 2047, 128, True),
+                                          (3, 6, 2, 2130, 2130, 128, False), (1, 64, 8, 8192, 8192, 128, True),
+                                          (1, 64, 8, 32768, 32768, 128, True), (1, 64, 8, 1, 4096, 128, True),
+                                          (1, 16, 16, 8192, 8192, 64, True), (4, 16, 16, 1024, 1024, 64, True),
+                                          (1, 64, 8, 1024, 1024, 128, True)):
         base = fa.attn_bwd_qk_workspace_bytes(B, Hq, Hkv, Sq, Sk, D)
         got = fa.attn_bwd_qk_workspace_bytes_for(B, Hq, Hkv, Sq, Sk, D, causal, 0, 0)
-        assert got == base + _stored_ds_bytes(B, Hq, Sq, Sk, causal, 0, 0), (B, Hq, Sq, Sk, causal)
+        assert got == base + _stored_ds_bytes(B, Hq, Sq, Sk, D, causal, 0, 0), (B, Hq, Sq, Sk, D, causal)
     # the 64-head S = 4096 causal problem: tiles t = 0 .. 63 hold 2t + 2 key blocks
-    assert _stored_ds_bytes(1, 64, 4096, 4096, True, 0, 0) == 64 * 4160 * 4096
+    assert _stored_ds_bytes(1, 64, 4096, 4096, 128, True, 0, 0) == 64 * 4160 * 4096
     # S = 8192 would need 4.3 GB (> 4 GiB): no stored dS
-    assert _stored_ds_bytes(1, 64, 8192, 8192, True, 0, 0) == 0
+    assert _stored_ds_bytes(1, 64, 8192, 8192, 128, True, 0, 0) == 0
     assert fa.attn_bwd_qk_workspace_bytes_for(1, 64, 8, 8192, 8192, 128, True, 0, 0) == \
         fa.attn_bwd_qk_workspace_bytes(1, 64, 8, 8192, 8192, 128)
     # one decode-like query row against 4096 keys: one tile of all 128 key blocks per head
-    assert _stored_ds_bytes(1, 64, 1, 4096, True, 0, 0) == 64 * 128 * 4096
+    assert _stored_ds_bytes(1, 64, 1, 4096, 128, True, 0, 0) == 64 * 128 * 4096
+    # where it does not pay: D = 64, or fewer than 2048 keys
+    assert _stored_ds_bytes(1, 16, 8192, 8192, 64, True, 0, 0) == 0
+    assert _stored_ds_bytes(1, 64, 1024, 1024, 128, True, 0, 0) == 0
+    assert _stored_ds_bytes(1, 4, 33, 2047, 128, True, 0, 0) == 0 < _stored_ds_bytes(1, 4, 7, 2048, 128, True, 0, 0)
 
 
 P = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first

@@ -81,13 +81,13 @@ def test_graph_forward_backward_head_split():
 
 
 def test_graph_forward_backward_stored_ds():
-    """The same problem with a workspace sized by attn_bwd_qk_workspace_bytes_for: the backward runs
-    the delta rows, the dK/dV pass storing dS, and the dQ pass reading it (whose trailing
-    workgroups add the head-split partials)."""
+    """S = 2100 with a workspace sized by attn_bwd_qk_workspace_bytes_for: the backward runs the delta
+    rows, the dK/dV pass storing dS, and the dQ pass reading it (whose trailing workgroups add the
+    head-split partials)."""
     import torch
     import causal_attention_fa2_amd as fa
     fa.attn_set_launch_hook(None)
-    B, Hq, Hkv, S, D = 1, 8, 2, 1000, 128
+    B, Hq, Hkv, S, D = 1, 8, 2, 2100, 128
     say("graph: forward + backward (stored dS, head split)")
     q, k, v, do = _inputs("bf16", B, Hq, Hkv, S, S, D, 305)
     scale = 1.0 / math.sqrt(D)

@@ -1,10 +1,11 @@
-"""The bf16 backward with its stored dS (a workspace of attn_bwd_qk_workspace_bytes_for, masks
-without a window or sink keys) against the same call with the plain workspace, where dQ recomputes
+"""The bf16 backward with its stored dS (a workspace of attn_bwd_qk_workspace_bytes_for; masks
+without a window or sink keys, D = 128, at least 2048 keys) against the same call with the plain
+workspace, where dQ recomputes
 the score and dP tiles. dK and dV come from the same kernel with the same delta rows, so they must
 be the same bits; dQ differs only by the rounding of P before dS is formed, and both dQ are checked
-against the fp64 oracle. Shapes: ragged causal squares at D = 64 / 128, grouped and ungrouped heads,
+against the fp64 oracle. Shapes: ragged causal squares, grouped and ungrouped heads (3 per group),
 fewer queries than keys (rows at an offset that is not a multiple of 32), one query row, no causal
-mask, a head group split over several dK/dV workgroups.
+mask, head groups split over several dK/dV workgroups (whose partials the dQ launch adds).
 """
 import math
 
@@ -17,17 +18,16 @@ from gpu_util import GATES, assert_parity, download, say, upload
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # B, Hq, Hkv, Sq, Sk, D, causal
-    (1, 4, 2, 300, 300, 64, True),
-    (1, 8, 2, 1000, 1000, 128, True),
-    (2, 4, 4, 257, 257, 128, True),
-    (1, 4, 2, 200, 333, 128, True),
-    (1, 4, 2, 1, 300, 64, True),
-    (1, 2, 2, 33, 33, 128, True),
-    (1, 4, 2, 300, 300, 64, False),
-    (2, 6, 2, 130, 170, 128, False),
+    # B, Hq, Hkv, Sq, Sk, D, causal (the stored dS is used at D = 128 with at least 2048 keys)
+    (1, 2, 1, 2049, 2049, 128, True),
+    (1, 8, 2, 2200, 2200, 128, True),
+    (2, 3, 3, 2077, 2077, 128, True),
+    (1, 4, 2, 300, 2100, 128, True),
+    (1, 4, 2, 1, 2300, 128, True),
+    (1, 2, 2, 33, 2048, 128, True),
+    (1, 2, 1, 2050, 2050, 128, False),
+    (1, 3, 1, 130, 2170, 128, False),
 ]
-
 
 def _backward(q, k, v, o, lse, do, ws_bytes, causal, scale):
     import torch
