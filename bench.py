@@ -272,7 +272,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the shader clock takes about 20 steps of this load to settle: warm-up covers it by default
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="query heads in the CPU oracle sample (rounded to whole KV groups)")
