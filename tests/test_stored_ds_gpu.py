@@ -27,6 +27,9 @@ CASES = [
     (1, 2, 2, 33, 2048, 128, True),
     (1, 2, 1, 2050, 2050, 128, False),
     (1, 3, 1, 130, 2170, 128, False),
+    # enough workgroups for the dQ pass to take 4 heads of a KV group per workgroup (two head chunks
+    # per group), and a 4-way head split of the dK/dV pass
+    (4, 16, 2, 2048, 2048, 128, True),
 ]
 
 def _backward(q, k, v, o, lse, do, ws_bytes, causal, scale):
