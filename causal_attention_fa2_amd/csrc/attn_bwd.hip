@@ -21,8 +21,8 @@
 //      few workgroups to fill the GPU, the head group is split into `hs` parts whose fp32 partial
 //      sums go to the workspace and
 //   3. dkdv_reduce_kernel (attn_dkdv.hip) adds them in a fixed order (deterministic) and rounds to the element type.
-// With a stored dS (bf16, a mask without a window or sinks, a workspace with room for it; layout
-// at DsMap in launch.h) the order is bwd_prep_kernel (the delta and base-2 log-sum-exp rows), the
+// With a stored dS (bf16, the shapes ds_bytes in launch.h admits, a workspace with room for it;
+// layout at DsMap there) the order is bwd_prep_kernel (the delta and base-2 log-sum-exp rows), the
 // dK / dV pass, which also writes each dS block it forms, and dq_ds_kernel, which reads those
 // blocks for dQ = scale * dS K (no score or dP products in the dQ pass) and, in trailing
 // workgroups, adds the dK / dV head-part partials.
@@ -264,8 +264,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __re
 // Both operands come through transposing LDS reads: K^T as in dq_kernel, and dS^T (a lane per
 // query, 8 keys) from the block, whose chunk holds one key's values for 8 queries: within each
 // group of 16 lanes, lane s reads the four queries 16g + 4(s % 4) .. of key 4(s / 4) + .., i.e.
-// chunk g*64 + (s & 1)*32 + (key ^ 4*(2g + (s & 1))), bytes 8 * ((s >> 1) & 1) .. Every block of a
-// strip holds the exact dS of its pairs (zeros where the mask hides them), so no mask here.
+// chunk g*64 + (s & 1)*32 + (key ^ 4*(2g + (s & 1))), bytes 8 * ((s >> 1) & 1) .. Every block a
+// query block needs (key blocks 0 .. ds_strip_len - 1) holds the exact dS of its pairs (zeros where
+// the mask hides them), so no mask here.
 // Workgroups n_dq.. of the same launch add the dK / dV head-part partials of a split head group
 // (what dkdv_reduce_kernel does otherwise, the same sums in the same order): the short reduce
 // fills in behind the dQ workgroups instead of taking a launch of its own (a prefill chunk's

@@ -35,7 +35,7 @@ constexpr int kMaxDocs = 2047;
 // reads them back for dQ = dS K instead of recomputing S = Q K^T and dP = dO V^T (a third of its
 // matrix products; the pages' backward recomputes the score tiles, which is what the pass does
 // without the room). Masks without a window or sink keys only; which shapes: ds_bytes.
-// Which blocks: query block i (rows 32i .. 32i+31) needs key blocks 0 .. n(i)-1, n(i) =
+// Which blocks: query block i (rows 32i .. 32i+31) needs key blocks 0 .. n(i)-1 (its strip), n(i) =
 // min(nkb, i + c) (c = nkb without the causal mask: every key). Layout, per (batch, KV head):
 // one entry per 64-row query tile t and key block j < min(nkb, 2t + 1 + c) (the keys of the tile's
 // second block), entries in order of t then j; an entry holds the G query heads of the group in
