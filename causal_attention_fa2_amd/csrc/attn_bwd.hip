@@ -367,11 +367,13 @@ __global__ __launch_bounds__(256, 2) void dq_ds_kernel(const uint16_t* __restric
     const uint32_t dl = lds_addr(stg + KTile::kBytes + w * RB * 2048);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      // blocks outside the strip are not read back; their copy takes the region's first block
+      // blocks outside the strip are not read back; their copy takes the region's first block.
+      // Each block is read once: non-temporal loads (dQ 247 -> 213 us at S = 4096 against cached
+      // loads; the K tiles, which every workgroup of the group reads, stay cached)
       const int i = ib + rb;
       const char* src = ds_base + (in_strip(i, j) ? ds_block_off(dsm, bg, hg, i, j) : 0);
-      dma16_s(lane * 16, src, dl + rb * 2048);
-      dma16_s(lane * 16, src + 1024, dl + rb * 2048 + 1024);
+      dma16_s<true>(lane * 16, src, dl + rb * 2048);
+      dma16_s<true>(lane * 16, src + 1024, dl + rb * 2048 + 1024);
     }
   };
   issue(0, ring);

@@ -368,6 +368,8 @@ __device__ __forceinline__ uint32_t dma_lane_off() {
   return (uint32_t)(r * Tile::kRowBytes + ((pos ^ Tile::swz(r)) << 4));
 }
 // `sbase` must be the same for every lane of the wave; it is moved to scalar registers here.
+// NT: a non-temporal (streaming) load, for data read exactly once.
+template <bool NT = false>
 __device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
   // (readfirstlane returns int: both halves are taken back to uint32_t before widening, so the
   // low half is zero-extended, not sign-extended)
@@ -375,8 +377,13 @@ __device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
   const uint64_t sa = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sa), "s"(lds_base) : "memory", "m0");
+  if constexpr (NT) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(sa), "s"(lds_base) : "memory", "m0");
+  } else {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sa), "s"(lds_base) : "memory", "m0");
+  }
 }
 template <class E, int ROWS, int D, int NW>
 constexpr bool dma_fast_ok() {
